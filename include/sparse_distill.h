@@ -1,0 +1,148 @@
+/*
+ * sparse_distill.h -- C ABI of the MI355X (gfx950) CSA indexer-distillation library
+ * (libsparse_distill.so).
+ *
+ * The operations follow the DeepSeek-V4 compressed-sparse-attention (CSA) layer as the
+ * Primus PR "perf(deepseek-v4): fuse and enable the indexer distillation loss"
+ * describes it: one softmax per head over [sliding-window keys | top-k selected
+ * compressed pool rows | per-head sink]; the indexer (student) is trained by
+ * KL(target || softmax(indexer logits)) where the target is that softmax's
+ * conditional on the selected rows, summed over heads and L1-renormalised.
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is a DEVICE pointer owned by the caller, contiguous and
+ *     row-major in the shape given; the library allocates no device memory and keeps
+ *     no state beyond a thread-local error string.
+ *   - Work is enqueued on `stream` (0 = the null stream) and returns without waiting:
+ *     no host synchronisation, no device-to-host copy.  Launch errors are reported
+ *     through the return status; a fault inside a kernel surfaces at the caller's next
+ *     synchronisation.
+ *   - Host-side validation runs before any HIP call.  A rejected call returns a
+ *     non-zero status, enqueues nothing and sets sd_last_error().
+ *   - Results are deterministic: every reduction has a fixed order.
+ *   - A top-k slot k of row (b,t) is VALID iff 0 <= idx[b,t,k] < N.  -1 is the usual
+ *     padding value (MaxText PR "Add Indexer Loss [Deepseek v4]", review comments:
+ *     unused top-k slots hold -1); any other out-of-range value is treated the same.
+ *     Causality and segment membership of idx are the caller's contract.
+ *   - Element types of q / kwin / pool: SD_BF16 (bfloat16) or SD_F32 (float32); all
+ *     other arrays are float32 or int32 as stated.  Arithmetic is fp32 with fp32
+ *     accumulation of bf16 (or fp32) products.
+ */
+#ifndef SPARSE_DISTILL_H
+#define SPARSE_DISTILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    SD_OK = 0,
+    SD_ERR_NULL_ARG = 1,    /* a required pointer is NULL                         */
+    SD_ERR_BAD_SHAPE = 2,   /* a size is non-positive or sizes are inconsistent     */
+    SD_ERR_UNSUPPORTED = 3, /* valid request outside the shapes the kernels cover   */
+    SD_ERR_DTYPE = 4,       /* unknown element-type code                           */
+    SD_ERR_HIP = 5          /* the HIP runtime reported an error at launch          */
+};
+
+enum { SD_BF16 = 0, SD_F32 = 1 };
+
+/*
+ * window_lse -- log-mass of the non-compressed part of each head's joint softmax.
+ *
+ *   nc_lse[b,t,h] = log( sum_{j in win(t)} exp(scale * <q[b,t,h,:], kwin[b,j,:]>)
+ *                        + exp(sink[h]) )
+ *   win(t) = { j : max(0, t-W+1) <= j <= t  and  seg[b,j] == seg[b,t] }
+ *
+ * Defined by the Primus PR above, commit "fix: build the target from the layer's
+ * joint softmax, add the sliding-window LSE kernel": the sliding-window plus sink
+ * log-mass is carried into the target's denominator.  The window holds the W keys
+ * ending at and including t; the sink is a raw per-head logit (not scaled).
+ *
+ *   q      [B,S,H,D]  dtype           queries (one row per token and head)
+ *   kwin   [B,S,D]    dtype           sliding-window keys, shared by all heads
+ *   sink   [H]        float32 or NULL per-head sink logit; NULL drops the term
+ *   seg    [B,S]      int32 or NULL   packed-segment ids; NULL = one segment
+ *   nc_lse [B,S,H]    float32 out     natural-log mass (never -inf: j = t is in win(t))
+ * Limits: D % 32 == 0, D <= 512; H <= 64; 1 <= W <= 128.
+ */
+int window_lse(const void *q, const void *kwin, const float *sink, const int32_t *seg,
+               int B, int S, int H, int D, int W, float scale, int dtype, float *nc_lse,
+               hipStream_t stream);
+
+/*
+ * distill_target -- the KL target over each token's top-k compressed-pool rows.
+ *
+ *   c[h,k]   = scale * <q[b,t,h,:], pool[b, idx[b,t,k], :]>        for valid k
+ *   full_h   = log( sum_{valid k} exp(c[h,k]) + exp(nc_lse[b,t,h]) )
+ *   m_k      = sum_h exp(c[h,k] - full_h)
+ *   target[b,t,k] = m_k / max(sum_{valid k} m_k, l1_floor)   (valid k);  exactly 0 otherwise
+ *
+ * Defined by the Primus PR above, PR body "Why the target was wrong" and the
+ * joint-softmax commit: the target is the conditional, on the selected compressed
+ * entries, of the layer's single softmax over window keys, compressed entries and
+ * sink; the per-head share exp(compressed_lse - full_lse) is kept, heads are summed,
+ * and the row is L1-renormalised with a float32-tiny floor.  The pool rows are read
+ * through idx inside the kernel (commit "fuse the KL target and the KL tail into
+ * Triton kernels": no gathered [B,S,K,D] tensor exists).
+ *
+ *   q      [B,S,H,D] dtype            queries
+ *   pool   [B,N,D]   dtype            compressed rows, shared by all heads
+ *   idx    [B,S,K]   int32            top-k pool rows; invalid slots as above
+ *   nc_lse [B,S,H]   float32 or NULL  from window_lse; NULL = legacy per-branch target
+ *                                     (each head renormalised over its compressed part)
+ *   l1_floor         <= 0 selects FLT_MIN (2^-126); 1e-10 reproduces the legacy floor
+ *   target [B,S,K]   float32 out      a row with no valid slot is all zeros
+ * Limits: D % 32 == 0, D <= 512; H <= 64; K <= 1024.
+ */
+int distill_target(const void *q, const void *pool, const int32_t *idx, const float *nc_lse,
+                   int B, int S, int H, int D, int N, int K, float scale, float l1_floor,
+                   int dtype, float *target, hipStream_t stream);
+
+/*
+ * distill_kl_fwd_bwd -- KL(target || softmax(logits)) per row, fused with its gradient.
+ *
+ *   V       = valid slots of the row;  lse = log sum_{k in V} exp(logits_k)
+ *   kl_rows[b,t] = sum_{k in V, target_k > 0} target_k * (log target_k - logits_k + lse)
+ *   dlogits[b,t,k] = grad_scale * ((sum_{j in V} target_j) * exp(logits_k - lse) - target_k)
+ *                    for k in V;  exactly 0 for k not in V
+ *   stats[0] = sum of kl_rows over rows with V non-empty;  stats[1] = number of such rows
+ * A row with no valid slot gives kl 0 and gradient 0; logits at invalid slots are never
+ * read into the arithmetic (they may hold NaN).  A row whose valid logits are all -inf
+ * is outside the contract.
+ *
+ * Defined by the Primus PR above, commit "fuse the KL target and the KL tail into
+ * Triton kernels" (KL(attention || indexer) with an analytic backward that saves
+ * nothing beyond its inputs), and the MaxText PR "Add Indexer Loss [Deepseek v4]",
+ * review comments (log-softmax KL without epsilon, exact gradient Q - P) and
+ * Description (queries that see no completed block are shielded from the loss).
+ * grad_scale carries the loss coefficient and the mean's 1/count.
+ *
+ *   target, logits [B,S,K] float32;  idx [B,S,K] int32 (validity only, 0 <= idx < N)
+ *   kl_rows [B,S] float32 out;  dlogits [B,S,K] float32 out or NULL (forward only)
+ *   stats [2] float32 out
+ *   workspace: device scratch of distill_kl_workspace_bytes(B,S,K) bytes, owned by the
+ *   caller; its contents need no initialisation and are overwritten.  Calls that share
+ *   a workspace must be ordered (same stream).
+ * Limits: K <= 4096.
+ */
+size_t distill_kl_workspace_bytes(int B, int S, int K);
+int distill_kl_fwd_bwd(const float *target, const float *logits, const int32_t *idx,
+                       int B, int S, int K, int N, float grad_scale, float *kl_rows,
+                       float *dlogits, float *stats, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *sd_status_string(int status);
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char *sd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_DISTILL_H */

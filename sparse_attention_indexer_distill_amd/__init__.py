@@ -1,0 +1,220 @@
+"""MI355X (gfx950) CSA indexer-distillation path.
+
+A thin ctypes binding over ``libsparse_distill.so`` (C ABI: ``include/sparse_distill.h``).
+The functions carry the same names as the C entry points and only marshal arguments:
+they check devices, dtypes and shapes, make tensors contiguous, allocate outputs with
+torch, and pass raw device pointers plus torch's current HIP stream.  Every step of the
+computation runs in the library's kernels; there is no fallback.  If the library is
+not built, every call raises.
+
+Semantics (DeepSeek-V4 CSA layer; Primus PR "perf(deepseek-v4): fuse and enable the
+indexer distillation loss" and MaxText PR "Add Indexer Loss [Deepseek v4]"):
+  window_lse          log-mass of each head's sliding-window keys plus its sink
+  distill_target      joint-softmax KL target over each token's top-k pool rows
+  distill_kl_fwd_bwd  KL(target || softmax(indexer logits)) and its gradient
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["window_lse", "distill_target", "distill_kl_fwd_bwd", "distill_kl_workspace_bytes",
+           "csa_distill_layer", "library_path", "load_library", "SD_BF16", "SD_F32"]
+
+SD_OK, SD_ERR_NULL_ARG, SD_ERR_BAD_SHAPE, SD_ERR_UNSUPPORTED, SD_ERR_DTYPE, SD_ERR_HIP = range(6)
+SD_BF16, SD_F32 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsparse_distill.so")
+_lib = None
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libsparse_distill.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built: run `python -m sparse_attention_indexer_distill_amd.build` "
+                           "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.window_lse.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]
+    lib.window_lse.restype = _i
+    lib.distill_target.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _f, _i, _vp, _vp]
+    lib.distill_target.restype = _i
+    lib.distill_kl_workspace_bytes.argtypes = [_i, _i, _i]
+    lib.distill_kl_workspace_bytes.restype = ctypes.c_size_t
+    lib.distill_kl_fwd_bwd.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.distill_kl_fwd_bwd.restype = _i
+    lib.sd_status_string.argtypes = [_i]
+    lib.sd_status_string.restype = ctypes.c_char_p
+    lib.sd_last_error.argtypes = []
+    lib.sd_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str) -> None:
+    if status == SD_OK:
+        return
+    lib = load_library()
+    msg = f"{what}: {lib.sd_status_string(status).decode()}: {lib.sd_last_error().decode()}"
+    if status in (SD_ERR_NULL_ARG, SD_ERR_BAD_SHAPE, SD_ERR_DTYPE):
+        raise ValueError(msg)
+    if status == SD_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise RuntimeError(msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SD_BF16
+    if t.dtype == torch.float32:
+        return SD_F32
+    raise ValueError(f"q/kwin/pool must be bfloat16 or float32, got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str, device: torch.device) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t if t.is_contiguous() else t.contiguous()
+
+
+def _stream(device: torch.device, stream) -> int:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def window_lse(q: torch.Tensor, kwin: torch.Tensor, sink: Optional[torch.Tensor] = None,
+               seg: Optional[torch.Tensor] = None, *, W: int, scale: Optional[float] = None,
+               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """nc_lse [B,S,H] fp32: log-mass of the W window keys ending at t (same segment) plus sink."""
+    lib = load_library()
+    dev = q.device
+    q = _dev(q, "q", dev)
+    kwin = _dev(kwin, "kwin", dev)
+    B, S, H, D = q.shape
+    if kwin.shape != (B, S, D) or kwin.dtype != q.dtype:
+        raise ValueError(f"kwin must be [{B},{S},{D}] {q.dtype}, got {tuple(kwin.shape)} {kwin.dtype}")
+    if sink is not None:
+        sink = _dev(sink.detach().to(torch.float32), "sink", dev)
+        if sink.numel() != H:
+            raise ValueError(f"sink must hold {H} head values, got {sink.numel()}")
+    if seg is not None:
+        seg = _dev(seg.to(torch.int32), "seg", dev)
+        if seg.shape != (B, S):
+            raise ValueError(f"seg must be [{B},{S}]")
+    if out is None:
+        out = torch.empty((B, S, H), dtype=torch.float32, device=dev)
+    elif out.shape != (B, S, H) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B,S,H] tensor")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib.window_lse(_ptr(q), _ptr(kwin), _ptr(sink), _ptr(seg), B, S, H, D, int(W), scale,
+                        _dtype_code(q), _ptr(out), _stream(dev, stream))
+    _check(st, "window_lse")
+    return out
+
+
+def distill_target(q: torch.Tensor, pool: torch.Tensor, idx: torch.Tensor,
+                   nc_lse: Optional[torch.Tensor] = None, *, scale: Optional[float] = None,
+                   l1_floor: float = 0.0, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """KL target [B,S,K] fp32 (joint softmax over window+sink mass nc_lse and the selected
+    pool rows; nc_lse None = legacy per-branch target).  l1_floor <= 0 means float32 tiny."""
+    lib = load_library()
+    dev = q.device
+    q = _dev(q, "q", dev)
+    pool = _dev(pool, "pool", dev)
+    B, S, H, D = q.shape
+    if pool.dim() != 3 or pool.shape[0] != B or pool.shape[2] != D or pool.dtype != q.dtype:
+        raise ValueError(f"pool must be [{B},N,{D}] {q.dtype}, got {tuple(pool.shape)} {pool.dtype}")
+    N = pool.shape[1]
+    if idx.dim() != 3 or idx.shape[:2] != (B, S):
+        raise ValueError(f"idx must be [{B},{S},K]")
+    idx = _dev(idx.to(torch.int32), "idx", dev)
+    K = idx.shape[2]
+    if nc_lse is not None:
+        nc_lse = _dev(nc_lse.detach().to(torch.float32), "nc_lse", dev)
+        if nc_lse.shape != (B, S, H):
+            raise ValueError(f"nc_lse must be [{B},{S},{H}]")
+    if out is None:
+        out = torch.empty((B, S, K), dtype=torch.float32, device=dev)
+    elif out.shape != (B, S, K) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B,S,K] tensor")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib.distill_target(_ptr(q), _ptr(pool), _ptr(idx), _ptr(nc_lse), B, S, H, D, N, K, scale,
+                            float(l1_floor), _dtype_code(q), _ptr(out), _stream(dev, stream))
+    _check(st, "distill_target")
+    return out
+
+
+def distill_kl_workspace_bytes(B: int, S: int, K: int) -> int:
+    return int(load_library().distill_kl_workspace_bytes(B, S, K))
+
+
+def distill_kl_fwd_bwd(target: torch.Tensor, logits: torch.Tensor, idx: torch.Tensor, N: int, *,
+                       grad_scale: float = 1.0, want_grad: bool = True,
+                       kl_rows: Optional[torch.Tensor] = None, dlogits: Optional[torch.Tensor] = None,
+                       stats: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor], torch.Tensor]:
+    """Per-row KL(target || softmax over valid slots of logits), its gradient scaled by
+    grad_scale (or None when want_grad is False), and stats = (sum of KL over non-empty
+    rows, number of non-empty rows)."""
+    lib = load_library()
+    dev = target.device
+    target = _dev(target, "target", dev)
+    logits = _dev(logits, "logits", dev)
+    if target.dim() != 3 or logits.shape != target.shape or idx.shape != target.shape:
+        raise ValueError("target, logits and idx must share one [B,S,K] shape")
+    if target.dtype != torch.float32 or logits.dtype != torch.float32:
+        raise ValueError("target and logits must be float32")
+    idx = _dev(idx.to(torch.int32), "idx", dev)
+    B, S, K = target.shape
+    if kl_rows is None:
+        kl_rows = torch.empty((B, S), dtype=torch.float32, device=dev)
+    if want_grad and dlogits is None:
+        dlogits = torch.empty((B, S, K), dtype=torch.float32, device=dev)
+    if not want_grad:
+        dlogits = None
+    if stats is None:
+        stats = torch.empty(2, dtype=torch.float32, device=dev)
+    need = distill_kl_workspace_bytes(B, S, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.distill_kl_fwd_bwd(_ptr(target), _ptr(logits), _ptr(idx), B, S, K, int(N), float(grad_scale),
+                                _ptr(kl_rows), _ptr(dlogits), _ptr(stats), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(dev, stream))
+    _check(st, "distill_kl_fwd_bwd")
+    return kl_rows, dlogits, stats
+
+
+def csa_distill_layer(q, kwin, pool, idx, logits, sink=None, seg=None, *, W: int,
+                      scale: Optional[float] = None, grad_scale: float = 1.0, want_grad: bool = True,
+                      bufs: Optional[dict] = None, stream=None):
+    """One CSA layer's distillation step: window_lse -> distill_target -> distill_kl_fwd_bwd.
+    ``bufs`` may hold preallocated outputs (nc_lse, target, kl_rows, dlogits, stats, workspace).
+    Returns a dict with every output."""
+    bufs = {} if bufs is None else bufs
+    nc = window_lse(q, kwin, sink, seg, W=W, scale=scale, out=bufs.get("nc_lse"), stream=stream)
+    T = distill_target(q, pool, idx, nc, scale=scale, out=bufs.get("target"), stream=stream)
+    kl, dz, st = distill_kl_fwd_bwd(T, logits, idx, pool.shape[1], grad_scale=grad_scale, want_grad=want_grad,
+                                    kl_rows=bufs.get("kl_rows"), dlogits=bufs.get("dlogits"),
+                                    stats=bufs.get("stats"), workspace=bufs.get("workspace"), stream=stream)
+    return dict(nc_lse=nc, target=T, kl_rows=kl, dlogits=dz, stats=st)

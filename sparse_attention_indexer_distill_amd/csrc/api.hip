@@ -1,0 +1,113 @@
+// api.hip -- the C ABI (include/sparse_distill.h): argument validation, then one or two
+// kernel launches on the caller's stream.  Validation happens entirely on the host and
+// before any HIP call, so every rejection path is exercised without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/sparse_distill.h"
+#include "sd_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return SD_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(SD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int check_common(int dtype, int B, int S, int H, int D) {
+    if (dtype != SD_BF16 && dtype != SD_F32) return fail(SD_ERR_DTYPE, "unknown dtype code %d", dtype);
+    if (B <= 0 || S <= 0 || H <= 0 || D <= 0)
+        return fail(SD_ERR_BAD_SHAPE, "sizes must be positive (B=%d S=%d H=%d D=%d)", B, S, H, D);
+    if ((int64_t)B * S * H * D > ((int64_t)1 << 40)) return fail(SD_ERR_BAD_SHAPE, "q is too large");
+    if (D % 32 != 0 || D > sd::kMaxDim)
+        return fail(SD_ERR_UNSUPPORTED, "head dim D=%d must be a multiple of 32 and at most %d", D, sd::kMaxDim);
+    if (H > sd::kMaxHeads) return fail(SD_ERR_UNSUPPORTED, "H=%d heads exceeds the supported %d", H, sd::kMaxHeads);
+    return SD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sd_status_string(int status) {
+    switch (status) {
+        case SD_OK: return "SD_OK";
+        case SD_ERR_NULL_ARG: return "SD_ERR_NULL_ARG";
+        case SD_ERR_BAD_SHAPE: return "SD_ERR_BAD_SHAPE";
+        case SD_ERR_UNSUPPORTED: return "SD_ERR_UNSUPPORTED";
+        case SD_ERR_DTYPE: return "SD_ERR_DTYPE";
+        case SD_ERR_HIP: return "SD_ERR_HIP";
+        default: return "SD_ERR_UNKNOWN";
+    }
+}
+
+const char *sd_last_error(void) { return g_err; }
+
+int window_lse(const void *q, const void *kwin, const float *sink, const int32_t *seg, int B, int S, int H, int D,
+               int W, float scale, int dtype, float *nc_lse, hipStream_t stream) {
+    if (!q || !kwin || !nc_lse) return fail(SD_ERR_NULL_ARG, "window_lse: q, kwin and nc_lse are required");
+    int st = check_common(dtype, B, S, H, D);
+    if (st != SD_OK) return st;
+    if (W <= 0) return fail(SD_ERR_BAD_SHAPE, "window_lse: W=%d must be positive", W);
+    if (W > sd::kMaxWindow) return fail(SD_ERR_UNSUPPORTED, "window_lse: W=%d exceeds %d", W, sd::kMaxWindow);
+    if (!isfinite(scale)) return fail(SD_ERR_BAD_SHAPE, "window_lse: scale must be finite");
+    return hip_status(sd::launch_window_lse(q, kwin, sink, seg, B, S, H, D, W, scale, dtype, nc_lse, stream),
+                      "window_lse launch");
+}
+
+int distill_target(const void *q, const void *pool, const int32_t *idx, const float *nc_lse, int B, int S, int H,
+                   int D, int N, int K, float scale, float l1_floor, int dtype, float *target, hipStream_t stream) {
+    if (!q || !pool || !idx || !target)
+        return fail(SD_ERR_NULL_ARG, "distill_target: q, pool, idx and target are required");
+    int st = check_common(dtype, B, S, H, D);
+    if (st != SD_OK) return st;
+    if (N <= 0 || K <= 0) return fail(SD_ERR_BAD_SHAPE, "distill_target: N=%d and K=%d must be positive", N, K);
+    if (K > sd::kMaxTopK) return fail(SD_ERR_UNSUPPORTED, "distill_target: K=%d exceeds %d", K, sd::kMaxTopK);
+    if (!isfinite(scale) || isnan(l1_floor))
+        return fail(SD_ERR_BAD_SHAPE, "distill_target: scale must be finite and l1_floor not NaN");
+    return hip_status(sd::launch_distill_target(q, pool, idx, nc_lse, B, S, H, D, N, K, scale, l1_floor, dtype,
+                                                target, stream),
+                      "distill_target launch");
+}
+
+size_t distill_kl_workspace_bytes(int B, int S, int K) {
+    if (B <= 0 || S <= 0 || K <= 0) return 0;
+    return sd::kl_workspace_bytes(B, S, K);
+}
+
+int distill_kl_fwd_bwd(const float *target, const float *logits, const int32_t *idx, int B, int S, int K, int N,
+                       float grad_scale, float *kl_rows, float *dlogits, float *stats, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+    if (!target || !logits || !idx || !kl_rows || !stats || !workspace)
+        return fail(SD_ERR_NULL_ARG, "distill_kl_fwd_bwd: target, logits, idx, kl_rows, stats and workspace are required");
+    if (B <= 0 || S <= 0 || K <= 0 || N <= 0)
+        return fail(SD_ERR_BAD_SHAPE, "distill_kl_fwd_bwd: sizes must be positive (B=%d S=%d K=%d N=%d)", B, S, K, N);
+    if (K > sd::kMaxKlK) return fail(SD_ERR_UNSUPPORTED, "distill_kl_fwd_bwd: K=%d exceeds %d", K, sd::kMaxKlK);
+    if ((int64_t)B * S > ((int64_t)1 << 31) - 4)
+        return fail(SD_ERR_UNSUPPORTED, "distill_kl_fwd_bwd: B*S too large");
+    if (!isfinite(grad_scale)) return fail(SD_ERR_BAD_SHAPE, "distill_kl_fwd_bwd: grad_scale must be finite");
+    const size_t need = sd::kl_workspace_bytes(B, S, K);
+    if (workspace_bytes < need)
+        return fail(SD_ERR_BAD_SHAPE, "distill_kl_fwd_bwd: workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    return hip_status(sd::launch_distill_kl(target, logits, idx, B, S, K, N, grad_scale, kl_rows, dlogits, stats,
+                                            workspace, stream),
+                      "distill_kl_fwd_bwd launch");
+}
+
+}  // extern "C"

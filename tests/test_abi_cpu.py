@@ -1,0 +1,130 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the header
+declares, and rejects bad arguments on the host with the documented status codes.
+
+Every call below is invalid on purpose, so the library returns before any HIP call;
+no kernel is ever launched from this file (the pointers are placeholders)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_attention_indexer_distill_amd as sd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_distill.h")
+FAKE = ctypes.c_void_p(0x1000)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sd.library_path()):
+        from sparse_attention_indexer_distill_amd import build
+        build.build()
+    return sd.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \t\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("window_lse", "distill_target", "distill_kl_fwd_bwd", "distill_kl_workspace_bytes",
+              "sd_status_string", "sd_last_error"):
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", sd.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in declared_functions():
+        assert n in exported, f"{n} not exported"
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    assert lib.sd_status_string(0) == b"SD_OK"
+    assert lib.sd_status_string(3) == b"SD_ERR_UNSUPPORTED"
+    assert lib.sd_status_string(99) == b"SD_ERR_UNKNOWN"
+
+
+def _wl(lib, q=FAKE, k=FAKE, out=FAKE, B=1, S=8, H=4, D=32, W=4, scale=0.1, dtype=0):
+    return lib.window_lse(q, k, None, None, B, S, H, D, W, scale, dtype, out, None)
+
+
+def test_window_lse_rejections(lib):
+    assert _wl(lib, q=None) == sd.SD_ERR_NULL_ARG
+    assert b"required" in lib.sd_last_error()
+    assert _wl(lib, out=None) == sd.SD_ERR_NULL_ARG
+    assert _wl(lib, B=0) == sd.SD_ERR_BAD_SHAPE
+    assert _wl(lib, S=-1) == sd.SD_ERR_BAD_SHAPE
+    assert _wl(lib, W=0) == sd.SD_ERR_BAD_SHAPE
+    assert _wl(lib, scale=float("inf")) == sd.SD_ERR_BAD_SHAPE
+    assert _wl(lib, dtype=7) == sd.SD_ERR_DTYPE
+    assert _wl(lib, D=48) == sd.SD_ERR_UNSUPPORTED
+    assert _wl(lib, D=544) == sd.SD_ERR_UNSUPPORTED
+    assert _wl(lib, H=65) == sd.SD_ERR_UNSUPPORTED
+    assert _wl(lib, W=129) == sd.SD_ERR_UNSUPPORTED
+    assert b"W=129" in lib.sd_last_error()
+
+
+def _tg(lib, q=FAKE, pool=FAKE, idx=FAKE, out=FAKE, B=1, S=8, H=4, D=32, N=2, K=4, scale=0.1, floor=0.0, dtype=0):
+    return lib.distill_target(q, pool, idx, None, B, S, H, D, N, K, scale, floor, dtype, out, None)
+
+
+def test_distill_target_rejections(lib):
+    assert _tg(lib, pool=None) == sd.SD_ERR_NULL_ARG
+    assert _tg(lib, idx=None) == sd.SD_ERR_NULL_ARG
+    assert _tg(lib, out=None) == sd.SD_ERR_NULL_ARG
+    assert _tg(lib, N=0) == sd.SD_ERR_BAD_SHAPE
+    assert _tg(lib, K=0) == sd.SD_ERR_BAD_SHAPE
+    assert _tg(lib, H=0) == sd.SD_ERR_BAD_SHAPE
+    assert _tg(lib, floor=float("nan")) == sd.SD_ERR_BAD_SHAPE
+    assert _tg(lib, dtype=-1) == sd.SD_ERR_DTYPE
+    assert _tg(lib, K=1025) == sd.SD_ERR_UNSUPPORTED
+    assert _tg(lib, D=16) == sd.SD_ERR_UNSUPPORTED
+    assert _tg(lib, H=128) == sd.SD_ERR_UNSUPPORTED
+
+
+def _kl(lib, T=FAKE, z=FAKE, idx=FAKE, B=1, S=8, K=4, N=2, g=1.0, rows=FAKE, dz=FAKE, st=FAKE, ws=FAKE,
+        wsb=1 << 20):
+    return lib.distill_kl_fwd_bwd(T, z, idx, B, S, K, N, g, rows, dz, st, ws, wsb, None)
+
+
+def test_distill_kl_rejections(lib):
+    assert lib.distill_kl_workspace_bytes(1, 8, 4) == 2 * 2 * 4
+    assert lib.distill_kl_workspace_bytes(0, 8, 4) == 0
+    assert _kl(lib, T=None) == sd.SD_ERR_NULL_ARG
+    assert _kl(lib, rows=None) == sd.SD_ERR_NULL_ARG
+    assert _kl(lib, st=None) == sd.SD_ERR_NULL_ARG
+    assert _kl(lib, ws=None) == sd.SD_ERR_NULL_ARG
+    assert _kl(lib, N=0) == sd.SD_ERR_BAD_SHAPE
+    assert _kl(lib, g=float("nan")) == sd.SD_ERR_BAD_SHAPE
+    assert _kl(lib, wsb=15) == sd.SD_ERR_BAD_SHAPE
+    assert b"workspace" in lib.sd_last_error()
+    assert _kl(lib, K=4097) == sd.SD_ERR_UNSUPPORTED
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 8, 4, 32, dtype=torch.bfloat16)
+    k = torch.zeros(1, 8, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        sd.window_lse(q, k, None, None, W=4)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        sd.distill_target(q, torch.zeros(1, 2, 32, dtype=torch.bfloat16), torch.zeros(1, 8, 4, dtype=torch.int32))
+
+
+def test_binding_maps_status_codes_to_exceptions(lib):
+    assert _wl(lib, D=48) == sd.SD_ERR_UNSUPPORTED
+    with pytest.raises(NotImplementedError, match="SD_ERR_UNSUPPORTED"):
+        sd._check(sd.SD_ERR_UNSUPPORTED, "window_lse")
+    with pytest.raises(ValueError):
+        sd._check(sd.SD_ERR_BAD_SHAPE, "x")
+    with pytest.raises(RuntimeError):
+        sd._check(sd.SD_ERR_HIP, "x")

@@ -1,0 +1,361 @@
+"""GPU parity of the HIP path against the fp64 oracle (needs an MI355X).
+
+Tolerances (stated once, used everywhere):
+  target T           abs 1e-5                       (the accuracy bar for target probabilities)
+  nc_lse             abs 1e-4 + rel 1e-5            (fp32 dot products over D <= 512 terms
+                                                     of magnitude ~1, scaled by 1/sqrt(D): ~1e-6
+                                                     typical error; the LSE adds |lse| * 2^-24)
+  KL per row         rel 1e-4 + abs 2e-6            (rel 1e-4 on loss and gradient; the absolute
+                                                     term covers rows whose KL is ~0, where fp32
+                                                     rounding of log T and z, ~1e-7 * |log T| per
+                                                     slot, is all that is left)
+  dlogits            per row: max|d| <= 1e-4 * max|ref| + 1e-6 * |g| * max_k T_k
+                                                    (norm-wise rel 1e-4; the absolute term is
+                                                     ~16 fp32 ulps of the row's largest
+                                                     probability, for rows where the student
+                                                     matches the target and the gradient is a
+                                                     difference of two nearly equal numbers)
+  loss (mean over non-empty rows) rel 1e-4; non-empty row count exact
+Masks and zero patterns are compared bit-exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+T_ATOL = 1e-5
+NC_ATOL, NC_RTOL = 1e-4, 1e-5
+KL_RTOL, KL_ATOL = 1e-4, 2e-6
+DZ_RTOL = 1e-4
+
+
+def _sd():
+    import sparse_attention_indexer_distill_amd as sd
+    sd.load_library()
+    return sd
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _dev():
+    return torch.device("cuda:0")
+
+
+def _to(x, dev):
+    return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+# ------------------------------------------------------------------ comparisons
+def check_T(T_gpu, T_ref, idx_rows, N, what):
+    """T_gpu, T_ref: [rows, K]; idx_rows [rows, K]."""
+    valid = (idx_rows >= 0) & (idx_rows < N)
+    # bit-exact zero pattern on invalid slots, and no NaN anywhere
+    assert np.isfinite(T_gpu).all(), f"{what}: non-finite target"
+    assert (T_gpu[~valid] == 0).all() and not np.signbit(T_gpu[~valid]).any(), f"{what}: invalid slot not +0"
+    err = np.abs(T_gpu - T_ref).max(initial=0.0)
+    assert err <= T_ATOL, f"{what}: max |T - T_ref| = {err:.3e}"
+    return err
+
+
+def check_nc(nc_gpu, nc_ref, what):
+    assert np.isfinite(nc_gpu).all(), f"{what}: non-finite nc_lse"
+    err = np.abs(nc_gpu - nc_ref)
+    bad = err > NC_ATOL + NC_RTOL * np.abs(nc_ref)
+    assert not bad.any(), f"{what}: nc_lse max err {err.max():.3e}"
+    return err.max(initial=0.0)
+
+
+def check_kl(kl_gpu, dz_gpu, kl_ref, dz_ref, idx_rows, N, what, T_rows, grad_scale=1.0):
+    valid = (idx_rows >= 0) & (idx_rows < N)
+    assert np.isfinite(kl_gpu).all() and np.isfinite(dz_gpu).all(), f"{what}: non-finite KL/grad"
+    assert (dz_gpu[~valid] == 0).all() and not np.signbit(dz_gpu[~valid]).any(), f"{what}: invalid slot grad not +0"
+    empty = ~valid.any(-1)
+    assert (kl_gpu[empty] == 0).all() and (dz_gpu[empty] == 0).all(), f"{what}: empty rows not zero"
+    e_kl = np.abs(kl_gpu - kl_ref)
+    assert (e_kl <= KL_RTOL * np.abs(kl_ref) + KL_ATOL).all(), f"{what}: KL err {e_kl.max():.3e}"
+    e_dz = np.abs(dz_gpu - dz_ref).max(-1)
+    scale = np.abs(dz_ref).max(-1)
+    atol = 1e-6 * abs(grad_scale) * np.abs(T_rows).max(-1)
+    assert (e_dz <= DZ_RTOL * scale + atol).all(), f"{what}: grad err {(e_dz / np.maximum(scale, 1e-30)).max():.3e}"
+    return e_kl.max(initial=0.0), (e_dz / np.maximum(scale, 1e-30)).max(initial=0.0)
+
+
+# ------------------------------------------------------------------ the layer on a config
+def run_config(name, nsample=None, shuffle_pad=False):
+    sd = _sd()
+    x = synth.make_inputs(name, shuffle_pad=shuffle_pad)
+    c = x["cfg"]
+    dev = _dev()
+    rows = np.arange(c.B * c.S) if nsample is None else synth.sample_rows(c, nsample)
+    idx_all = x["idx"].reshape(-1, c.K).numpy()
+    # c4-style rows whose student logits equal log(target)
+    z = x["z"].clone()
+    if len(x["kl_zero_rows"]):
+        Tz = oracle.target(x["q"], x["pool"], x["idx"], x["kwin"], x["sink"], x["seg"], W=c.W,
+                           scale=c.scale, rows=x["kl_zero_rows"]).astype(np.float32)
+        with np.errstate(divide="ignore"):
+            zz = np.where(Tz > 0, np.log(np.where(Tz > 0, Tz, 1.0)), -60.0).astype(np.float32)
+        z.reshape(-1, c.K)[torch.as_tensor(x["kl_zero_rows"])] = torch.from_numpy(zz)
+    g = _to(x, dev)
+    g["z"] = z.to(dev)
+    _say(f"[gpu] {name}: layer B={c.B} S={c.S} H={c.H} D={c.D} N={c.N} K={c.K} W={c.W} {c.dtype}")
+    out = sd.csa_distill_layer(g["q"], g["kwin"], g["pool"], g["idx"], g["z"], g["sink"], g["seg"], W=c.W,
+                               grad_scale=1.0)
+    torch.cuda.synchronize()
+    nc = _np(out["nc_lse"]).reshape(-1, c.H)[rows]
+    T = _np(out["target"]).reshape(-1, c.K)[rows]
+    kl = _np(out["kl_rows"]).reshape(-1)[rows]
+    dz = _np(out["dlogits"]).reshape(-1, c.K)[rows]
+    stats = _np(out["stats"])
+    # oracle on the same rows
+    nc_ref = oracle.window_lse(x["q"], x["kwin"], x["sink"], x["seg"], c.W, c.scale, rows=rows)
+    T_ref = oracle.target(x["q"], x["pool"], x["idx"], x["kwin"], x["sink"], x["seg"], W=c.W, scale=c.scale,
+                          rows=rows)
+    z_rows = z.reshape(-1, c.K).numpy()[rows]
+    kl_ref, dz_ref, _ = oracle.kl(T_ref.astype(np.float32), z_rows, idx_all[rows], c.N)
+    e_nc = check_nc(nc, nc_ref, name)
+    e_T = check_T(T, T_ref, idx_all[rows], c.N, name)
+    e_kl, e_dz = check_kl(kl, dz, kl_ref, dz_ref, idx_all[rows], c.N, name, T_ref)
+    # loss statistics: the count is exact, the sum is checked when every row was compared
+    nonempty = ((idx_all >= 0) & (idx_all < c.N)).any(-1)
+    assert stats[1] == nonempty.sum()
+    if nsample is None:
+        assert abs(stats[0] - kl_ref[nonempty[rows]].sum()) <= KL_RTOL * abs(kl_ref.sum()) + 1e-5
+    else:
+        kl_all = _np(out["kl_rows"]).reshape(-1).astype(np.float64)
+        assert abs(stats[0] - kl_all[nonempty].sum()) <= 1e-5 * abs(kl_all.sum()) + 1e-5
+    _say(f"[gpu] {name}: max err nc {e_nc:.2e} T {e_T:.2e} KL {e_kl:.2e} grad(rel) {e_dz:.2e} "
+         f"rows {len(rows)} stats {stats.tolist()}")
+    return x, out, rows
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c1_local"])
+def test_layer_parity_all_rows(name):
+    run_config(name)
+
+
+@pytest.mark.parametrize("name", ["c3", "c4", "c3_local", "c5"])
+def test_layer_parity_full_size_sampled(name):
+    x, out, rows = run_config(name, nsample=48)
+    c = x["cfg"]
+    if len(x["kl_zero_rows"]):
+        kl = _np(out["kl_rows"]).reshape(-1)[x["kl_zero_rows"]]
+        assert np.abs(kl).max() <= 1e-5, f"KL on rows with student = log target: {np.abs(kl).max():.3e}"
+    if name == "c3_local":
+        # every non-empty row renormalises to 1 although its compressed mass is < 1e-10
+        T = _np(out["target"]).reshape(-1, c.K)
+        idx = x["idx"].reshape(-1, c.K).numpy()
+        ne = ((idx >= 0) & (idx < c.N)).any(-1)
+        np.testing.assert_allclose(T[ne].sum(-1), 1.0, atol=1e-4)
+
+
+def test_shuffled_padding_parity():
+    run_config("c2", shuffle_pad=True)
+
+
+# ------------------------------------------------------------------ isolated kernels
+def test_target_isolated_with_given_nc_lse_and_legacy():
+    sd = _sd()
+    dev = _dev()
+    for name in ("c1", "c2"):
+        x = synth.make_inputs(name, shuffle_pad=True)
+        c = x["cfg"]
+        nc_ref = oracle.window_lse(x["q"], x["kwin"], x["sink"], x["seg"], c.W, c.scale)
+        nc32 = torch.from_numpy(nc_ref.astype(np.float32)).reshape(c.B, c.S, c.H)
+        g = _to(x, dev)
+        _say(f"[gpu] {name}: target with oracle nc_lse, and legacy")
+        T = sd.distill_target(g["q"], g["pool"], g["idx"], nc32.to(dev))
+        Tl = sd.distill_target(g["q"], g["pool"], g["idx"], None, l1_floor=1e-10)
+        torch.cuda.synchronize()
+        T_ref = oracle.target(x["q"], x["pool"], x["idx"], nc_lse=nc32.reshape(-1, c.H).double().numpy(),
+                              scale=c.scale)
+        Tl_ref = oracle.target(x["q"], x["pool"], x["idx"], scale=c.scale, floor=1e-10)
+        idx = x["idx"].reshape(-1, c.K).numpy()
+        check_T(_np(T).reshape(-1, c.K), T_ref, idx, c.N, name + " given nc")
+        check_T(_np(Tl).reshape(-1, c.K), Tl_ref, idx, c.N, name + " legacy")
+
+
+def test_local_dominant_floor_on_gpu():
+    """Local-dominant rows: float32-tiny floor renormalises to 1, the legacy floor clips."""
+    sd = _sd()
+    dev = _dev()
+    x = synth.make_inputs("c1_local")
+    c = x["cfg"]
+    g = _to(x, dev)
+    _say("[gpu] c1_local: floors")
+    nc = sd.window_lse(g["q"], g["kwin"], g["sink"], g["seg"], W=c.W)
+    T = _np(sd.distill_target(g["q"], g["pool"], g["idx"], nc)).reshape(-1, c.K)
+    Tl = _np(sd.distill_target(g["q"], g["pool"], g["idx"], nc, l1_floor=1e-10)).reshape(-1, c.K)
+    idx = x["idx"].reshape(-1, c.K).numpy()
+    ne = ((idx >= 0) & (idx < c.N)).any(-1)
+    np.testing.assert_allclose(T[ne].sum(-1), 1.0, atol=1e-5)
+    assert (Tl[ne].sum(-1) < 1e-3).all()
+    mass_ref = oracle.target(x["q"], x["pool"], x["idx"], x["kwin"], x["sink"], x["seg"], W=c.W,
+                             scale=c.scale, floor=1.0).sum(-1)
+    np.testing.assert_allclose(Tl[ne].sum(-1), mass_ref[ne] / 1e-10, rtol=1e-3)
+
+
+def test_kl_isolated_all_configs():
+    """KL kernel alone on oracle-independent inputs: T is a normalised random row."""
+    sd = _sd()
+    dev = _dev()
+    for name in ("c1", "c2", "c3", "c5"):
+        x = synth.make_inputs(name) if name in ("c1", "c2") else None
+        c = synth.CONFIGS[name]
+        idx = x["idx"] if x is not None else torch.from_numpy(synth.topk_slots(c, synth.rng_for(c, "idx")))
+        rng = np.random.default_rng(c.cid)
+        valid = ((idx >= 0) & (idx < c.N)).numpy()
+        r = rng.random(idx.shape).astype(np.float32) * valid
+        s = r.sum(-1, keepdims=True)
+        T = np.where(s > 0, r / np.where(s > 0, s, 1), 0).astype(np.float32)
+        z = rng.standard_normal(idx.shape).astype(np.float32)
+        z[~valid] = np.nan                                   # never read into the arithmetic
+        _say(f"[gpu] {name}: KL isolated")
+        kl, dz, st = sd.distill_kl_fwd_bwd(torch.from_numpy(T).to(dev), torch.from_numpy(z).to(dev),
+                                           idx.to(dev), c.N, grad_scale=0.5)
+        torch.cuda.synchronize()
+        kl_ref, dz_ref, st_ref = oracle.kl(T, z, idx, c.N, grad_scale=0.5)
+        check_kl(_np(kl).reshape(-1), _np(dz).reshape(-1, c.K), kl_ref, dz_ref, idx.reshape(-1, c.K).numpy(),
+                 c.N, name, T.reshape(-1, c.K), grad_scale=0.5)
+        stn = _np(st)
+        assert stn[1] == st_ref[1]
+        assert abs(stn[0] - st_ref[0]) <= KL_RTOL * abs(st_ref[0])
+        # forward-only call gives the same forward numbers
+        kl2, dz2, st2 = sd.distill_kl_fwd_bwd(torch.from_numpy(T).to(dev), torch.from_numpy(z).to(dev),
+                                              idx.to(dev), c.N, want_grad=False)
+        assert dz2 is None
+        assert torch.equal(kl2, kl) and torch.equal(st2, st)
+
+
+# ------------------------------------------------------------------ edge shapes
+EDGE = [
+    # (name, B, S, H, D, N, K, W, dtype, segments)
+    ("ragged", 2, 37, 5, 64, 9, 13, 6, "bf16", 1),
+    ("k1_sparse", 1, 40, 16, 32, 10, 1, 3, "bf16", 1),
+    ("w1", 1, 24, 3, 32, 6, 4, 1, "f32", 1),
+    ("w_gt_s", 1, 20, 16, 32, 5, 6, 128, "bf16", 1),
+    ("h20_d96", 1, 50, 20, 96, 12, 20, 17, "bf16", 2),
+    ("h64_k1024", 1, 64, 64, 512, 16, 1024, 128, "bf16", 1),
+    ("all_empty", 1, 3, 4, 32, 4, 4, 2, "f32", 1),
+    ("f32_h64", 1, 48, 64, 128, 12, 40, 33, "f32", 1),
+    ("k_gt_blocks", 2, 44, 8, 32, 11, 300, 20, "bf16", 1),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda e: e[0])
+def test_edge_shapes(case):
+    name, B, S, H, D, N, K, W, dt, segs = case
+    cid = 800 + EDGE.index(case)
+    if segs > 1:
+        S = (S // (4 * segs)) * 4 * segs
+        N = S // 4
+    cfg = synth.Config(name, cid, B=B, S=S, H=H, D=D, N=N, K=K, W=W, dtype=dt, segments=segs)
+    sd = _sd()
+    dev = _dev()
+    x = synth.make_inputs(cfg, shuffle_pad=True)
+    g = _to(x, dev)
+    _say(f"[gpu] edge {name}: B={B} S={S} H={H} D={D} N={N} K={K} W={W} {dt} segs={segs}")
+    out = sd.csa_distill_layer(g["q"], g["kwin"], g["pool"], g["idx"], g["z"], g["sink"], g["seg"], W=W,
+                               grad_scale=1.0)
+    torch.cuda.synchronize()
+    nc_ref = oracle.window_lse(x["q"], x["kwin"], x["sink"], x["seg"], W, cfg.scale)
+    T_ref = oracle.target(x["q"], x["pool"], x["idx"], x["kwin"], x["sink"], x["seg"], W=W, scale=cfg.scale)
+    idx = x["idx"].reshape(-1, K).numpy()
+    kl_ref, dz_ref, _ = oracle.kl(T_ref.astype(np.float32), x["z"], x["idx"], N)
+    check_nc(_np(out["nc_lse"]).reshape(-1, H), nc_ref, name)
+    check_T(_np(out["target"]).reshape(-1, K), T_ref, idx, N, name)
+    check_kl(_np(out["kl_rows"]).reshape(-1), _np(out["dlogits"]).reshape(-1, K), kl_ref, dz_ref, idx, N, name,
+             T_ref)
+
+
+# ------------------------------------------------------------------ poison, isolation, determinism
+def test_poison_unreferenced_inputs_leave_outputs_bitwise_unchanged():
+    sd = _sd()
+    dev = _dev()
+    cfg = synth.Config("poison", 851, B=1, S=256, H=16, D=128, N=64, K=16, W=20, dtype="bf16", segments=2)
+    x = synth.make_inputs(cfg, shuffle_pad=True)
+    idx = x["idx"].clone()
+    # (a) drop every reference to a set of pool rows, then poison those rows
+    dropped = torch.tensor([0, 5, 17, 40, 63])
+    idx[torch.isin(idx, dropped)] = -1
+    g = _to(x, dev)
+    g["idx"] = idx.to(dev)
+    _say("[gpu] poison: clean run")
+    ref = sd.csa_distill_layer(g["q"], g["kwin"], g["pool"], g["idx"], g["z"], g["sink"], g["seg"], W=cfg.W)
+    pool_p = g["pool"].clone()
+    pool_p[:, dropped] = float("nan")
+    # (b) keys of segment 0 poisoned: tokens of segment 1 must not see them
+    kwin_p = g["kwin"].clone()
+    kwin_p[:, : cfg.S // 2] = float("inf")
+    # (c) student logits at invalid slots poisoned
+    z_p = g["z"].clone()
+    z_p[~((g["idx"] >= 0) & (g["idx"] < cfg.N))] = float("nan")
+    _say("[gpu] poison: poisoned run")
+    out = sd.csa_distill_layer(g["q"], kwin_p, pool_p, g["idx"], z_p, g["sink"], g["seg"], W=cfg.W)
+    torch.cuda.synchronize()
+    h = cfg.S // 2
+    assert torch.equal(out["nc_lse"][:, h:], ref["nc_lse"][:, h:])
+    assert torch.isfinite(out["target"][:, h:]).all()
+    # pool poison only touches unreferenced rows: targets of every token bitwise equal
+    T2 = sd.distill_target(g["q"], pool_p, g["idx"], ref["nc_lse"])
+    assert torch.equal(T2, ref["target"])
+    kl2, dz2, st2 = sd.distill_kl_fwd_bwd(ref["target"], z_p, g["idx"], cfg.N)
+    assert torch.equal(kl2, ref["kl_rows"]) and torch.equal(dz2, ref["dlogits"]) and torch.equal(st2, ref["stats"])
+
+
+def test_segment_isolation_perturbation():
+    sd = _sd()
+    dev = _dev()
+    x = synth.make_inputs("c4")
+    c = x["cfg"]
+    g = _to(x, dev)
+    _say("[gpu] c4: segment isolation")
+    nc = sd.window_lse(g["q"], g["kwin"], g["sink"], g["seg"], W=c.W)
+    k2 = g["kwin"].clone()
+    k2[:, : c.S // 2] = torch.randn_like(k2[:, : c.S // 2])
+    nc2 = sd.window_lse(g["q"], k2, g["sink"], g["seg"], W=c.W)
+    torch.cuda.synchronize()
+    assert torch.equal(nc[:, c.S // 2:], nc2[:, c.S // 2:])
+    assert not torch.equal(nc[:, : c.S // 2], nc2[:, : c.S // 2])
+
+
+def test_deterministic_bitwise():
+    sd = _sd()
+    dev = _dev()
+    x = synth.make_inputs("c3")
+    c = x["cfg"]
+    g = _to(x, dev)
+    _say("[gpu] c3: determinism")
+    a = sd.csa_distill_layer(g["q"], g["kwin"], g["pool"], g["idx"], g["z"], g["sink"], g["seg"], W=c.W)
+    a = {k: v.clone() for k, v in a.items()}
+    b = sd.csa_distill_layer(g["q"], g["kwin"], g["pool"], g["idx"], g["z"], g["sink"], g["seg"], W=c.W)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_binding_rejects_bad_arguments_on_gpu_tensors():
+    sd = _sd()
+    dev = _dev()
+    q = torch.zeros(1, 8, 4, 48, dtype=torch.bfloat16, device=dev)
+    k = torch.zeros(1, 8, 48, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(NotImplementedError):
+        sd.window_lse(q, k, None, None, W=4)                       # D=48 unsupported
+    q = torch.zeros(1, 8, 4, 64, dtype=torch.bfloat16, device=dev)
+    k = torch.zeros(1, 8, 64, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        sd.window_lse(q, k, torch.zeros(3, device=dev), None, W=4)  # sink size
+    with pytest.raises(ValueError):
+        sd.window_lse(q, k, None, None, W=0)
+    with pytest.raises(NotImplementedError):
+        sd.window_lse(q, k, None, None, W=129)

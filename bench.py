@@ -1,0 +1,228 @@
+"""Benchmark: ms per CSA layer of the indexer-distillation hot path on one MI355X.
+
+One step = window_lse -> distill_target -> distill_kl_fwd_bwd (forward and backward to the
+student logits) over one V4-Flash-shaped CSA layer (B=1, S=4096, H=64, D=512, pool N=1024,
+top-k K=512, window W=128; bf16 q / pool / window keys, fp32 sink and student logits,
+uniform causal top-k slots), with every input resident in HBM before the timed region.
+
+Prints ONE JSON line.  `value` is the wall-clock ms per layer over the timed steps
+(bracketed by device synchronisation).  Per-kernel durations come from HIP events recorded
+on the stream the kernels run on (torch's current stream), and give each kernel's
+achieved rate against its binding roofline (MI355X peaks: 2.5 PFLOP/s dense bf16 MFMA,
+8 TB/s HBM).  `cpu_baseline` times the fp64 oracle on a strided quarter of the rows.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+METRIC = "ms per CSA layer (target+window_lse+KL fwd/bwd), % MFMA/HBM roofline"
+KERNEL_SOURCES = {
+    "distill_target": "sparse_attention_indexer_distill_amd/csrc/distill_target.hip",
+    "window_lse": "sparse_attention_indexer_distill_amd/csrc/window_lse.hip",
+    "distill_kl_fwd_bwd": "sparse_attention_indexer_distill_amd/csrc/distill_kl.hip",
+}
+
+
+def src_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for p in (KERNEL_SOURCES[kernel], "sparse_attention_indexer_distill_amd/csrc/sd_device.hpp"):
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def window_pairs(cfg, seg) -> int:
+    """Number of (token, window key) pairs: sum_t |win(t)|."""
+    S, W = cfg.S, cfg.W
+    t = np.arange(S)
+    if seg is None:
+        return int(cfg.B * np.minimum(t + 1, W).sum())
+    total = 0
+    for b in range(cfg.B):
+        s = seg[b].numpy()
+        start = np.zeros(S, dtype=np.int64)       # first token of t's segment
+        for i in range(1, S):
+            start[i] = start[i - 1] if s[i] == s[i - 1] else i
+        total += int(np.minimum(t - start + 1, W).sum())
+    return total
+
+
+def algorithmic_work(cfg, x) -> dict:
+    B, S, H, D, N, K = cfg.B, cfg.S, cfg.H, cfg.D, cfg.N, cfg.K
+    e = 2 if cfg.dtype == "bf16" else 4
+    idx = x["idx"]
+    valid = int(((idx >= 0) & (idx < N)).sum())
+    wp = window_pairs(cfg, x["seg"])
+    seg_b = 0 if x["seg"] is None else B * S * 4
+    return {
+        "window_lse": dict(flops=2 * H * D * wp, bytes=B * S * H * D * e + B * S * D * e + B * S * H * 4 + H * 4 + seg_b,
+                           pairs=wp),
+        "distill_target": dict(flops=2 * H * D * valid,
+                               bytes=B * S * H * D * e + B * N * D * e + B * S * K * 4 + B * S * H * 4 + B * S * K * 4,
+                               pairs=valid),
+        "distill_kl_fwd_bwd": dict(flops=10 * valid, bytes=B * S * K * 4 * 4 + B * S * 4 + 8, pairs=valid),
+    }
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
+    summary is missing or was taken from a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"source sha256\[:16\]:\s*([0-9a-f]{16})", text)
+    m_b = re.search(r"HBM bytes per launch:\s*([0-9.eE+]+)", text)
+    if not m_src or not m_b or m_src.group(1) != src_hash(kernel):
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(cfg, x, kernels_s_per_layer: float) -> dict:
+    import oracle
+    rows = np.arange(0, cfg.B * cfg.S, 4)          # strided quarter of the rows
+    t0 = time.perf_counter()
+    oracle.window_lse(x["q"], x["kwin"], x["sink"], x["seg"], cfg.W, cfg.scale, rows=rows)
+    T = oracle.target(x["q"], x["pool"], x["idx"], x["kwin"], x["sink"], x["seg"], W=cfg.W, scale=cfg.scale,
+                      rows=rows)
+    oracle.kl(T.astype(np.float32), x["z"].reshape(-1, cfg.K).numpy()[rows],
+              x["idx"].reshape(-1, cfg.K).numpy()[rows], cfg.N)
+    dt = time.perf_counter() - t0
+    ms_layer = dt * 1e3 * (cfg.B * cfg.S) / len(rows)
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(ms_layer, 3), "unit": "ms", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{len(rows)} of {cfg.B * cfg.S} rows (every 4th), fp64 window_lse + joint target + KL; "
+                      f"{dt:.2f} s wall, scaled by {cfg.B * cfg.S / len(rows):.0f}x",
+            "cpu": cpu, "nproc": os.cpu_count(), "gpu_speedup": round(ms_layer / (kernels_s_per_layer * 1e3), 1)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3", choices=["c3", "c4", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB three times (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU only (the path runs on a single MI355X); got --gpus {args.gpus}. "
+              "Multi-GPU sharding of this path is a design note, not a measured configuration.", file=sys.stderr)
+        return 2
+
+    import sparse_attention_indexer_distill_amd as sd
+    sd.load_library()
+    cfg = synth.CONFIGS[args.workload]
+    x = synth.make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    B, S, H, K = cfg.B, cfg.S, cfg.H, cfg.K
+    bufs = dict(nc_lse=torch.empty(B, S, H, device=dev), target=torch.empty(B, S, K, device=dev),
+                kl_rows=torch.empty(B, S, device=dev), dlogits=torch.empty(B, S, K, device=dev),
+                stats=torch.empty(2, device=dev),
+                workspace=torch.empty(sd.distill_kl_workspace_bytes(B, S, K), dtype=torch.uint8, device=dev))
+    nonempty = int(((x["idx"] >= 0) & (x["idx"] < cfg.N)).any(-1).sum())
+    grad_scale = 1e-2 / nonempty          # loss coefficient 1e-2, mean over non-empty rows
+
+    names = ["window_lse", "distill_target", "distill_kl_fwd_bwd"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        sd.window_lse(g["q"], g["kwin"], g["sink"], g["seg"], W=cfg.W, out=bufs["nc_lse"])
+        if ev is not None:
+            ev[1].record()
+        sd.distill_target(g["q"], g["pool"], g["idx"], bufs["nc_lse"], out=bufs["target"])
+        if ev is not None:
+            ev[2].record()
+        sd.distill_kl_fwd_bwd(bufs["target"], g["z"], g["idx"], cfg.N, grad_scale=grad_scale,
+                              kl_rows=bufs["kl_rows"], dlogits=bufs["dlogits"], stats=bufs["stats"],
+                              workspace=bufs["workspace"])
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region 1: whole steps, wall clock between device synchronisations
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # timed region 2: the same steps with HIP events between the kernels (per-kernel time)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    per_min = {n: float(np.min([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+
+    work = algorithmic_work(cfg, x)
+    kernels = {}
+    for n in names:
+        ms = per[n]
+        tf = work[n]["flops"] / (ms * 1e-3) / 1e12
+        gbs = work[n]["bytes"] / (ms * 1e-3) / 1e9
+        kernels[n] = {"ms": round(ms, 4), "ms_min": round(per_min[n], 4), "TFLOP/s": round(tf, 1),
+                      "GB/s": round(gbs, 1), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                      "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                      "algorithmic_flops": work[n]["flops"], "algorithmic_bytes": work[n]["bytes"],
+                      "src": src_hash(n)}
+    dom = "distill_target"
+    ach = kernels[dom]["TFLOP/s"]
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": read_traffic(dom, args.workload)}
+    kern_total = sum(per.values()) * 1e-3
+    out = {
+        "metric": METRIC, "value": round(ms_per_step, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: V4-Flash-shaped CSA layer" if cfg.name == "c3" else cfg.name,
+                   "B": B, "S": S, "H": H, "D": cfg.D, "N": cfg.N, "K": K, "W": cfg.W,
+                   "global_batch": B, "seq_len": S, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "layer_useful_TFLOP/s": round(sum(w["flops"] for w in work.values()) / (ms_per_step * 1e-3) / 1e12, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, x, kern_total)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -13,8 +13,9 @@
 // staged once in LDS in MFMA fragment order.  The valid slots of the row are compacted
 // (stable, slot order) into a list in LDS; 16-slot tiles of that list are dealt
 // round-robin to the waves, so invalid (-1) slots cost no MFMA work wherever they sit.
-// Each wave streams its rows' fragments straight from L2/HBM (each lane reads 16
-// contiguous bytes of one pool row per 32-wide D chunk) and accumulates
+// Each wave streams its rows' fragments straight from L2 with buffer loads (each lane
+// reads 16 contiguous bytes of one pool row per 32-wide D chunk, one chunk ahead of the
+// MFMAs) and accumulates
 //     C[slot][head] (16x16 tiles) = pool_row . q_head
 // for all heads, keeping every score of its slots in registers.  The per-head maximum
 // and sum (log2 domain) need two cross-lane steps plus one LDS exchange between waves;
@@ -28,176 +29,270 @@
 namespace sd {
 namespace {
 
-template <int DT, int HT, int KT, int NW>
-__global__ __launch_bounds__(NW * 64) void distill_target_kernel(
-    const void *__restrict__ q, const void *__restrict__ pool, const int32_t *__restrict__ idx,
-    const float *__restrict__ nc_lse, int S, int H, int D, int N, int K, float scale_log2, float l1_floor,
-    float *__restrict__ target) {
+// Queries of one token in LDS: head row h at byte h*RS (RS = D*EB + 16: the 16-byte pad
+// makes the 16 rows of a fragment read fall in distinct banks).  A fragment unit for
+// (head tile ht, chunk c) is read at row 16*ht + l%16, byte (32c + 8*(l/16))*EB.
+__device__ __forceinline__ int qrow_stride(int D, int EB) { return D * EB + 16; }
+
+template <int DT, int HT>
+__device__ __forceinline__ typename Elem<DT>::frag_t q_frag(const unsigned char *qb, int RS, int ht, int c, int lane) {
+    constexpr int EB = Elem<DT>::bytes;
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(qb + (ht * 16 + (lane & 15)) * RS + (32 * c + 8 * (lane >> 4)) * EB);
+    if constexpr (DT == 0) {
+        return p[0];
+    } else {
+        const f32x4 lo = __builtin_bit_cast(f32x4, p[0]), hi = __builtin_bit_cast(f32x4, p[1]);
+        return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+}
+
+
+// Scores of MY slot tiles against all heads, streaming D in 32-element chunks.  The
+// gathered pool fragments (buffer loads) and the query fragments (LDS) of chunk c+1 are
+// in flight while chunk c's MFMAs run.  MY is a compile-time count, so the loop has no
+// per-tile branches.
+template <int DT, int HT, int MY, int KT>
+__device__ __forceinline__ void score_tiles(f32x4 (&acc)[KT][HT], const unsigned char *__restrict__ qb, int RS, rsrc_t pool,
+                                            const uint32_t (&off)[KT], int nch, int lane) {
     using frag_t = typename Elem<DT>::frag_t;
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int nch = D >> 5;
-    frag_t *qs = reinterpret_cast<frag_t *>(smem);                 // [HT][nch][64]
-    int32_t *crow = reinterpret_cast<int32_t *>(qs + (size_t)HT * nch * 64);  // [K] pool row per compacted slot
-    int32_t *cslot = crow + K;                                      // [K] slot index per compacted slot
-    float *red_a = reinterpret_cast<float *>(cslot + K);            // [NW][16*HT]
-    float *red_b = red_a + NW * 16 * HT;                            // [NW][16*HT]
-    float *red_t = red_b + NW * 16 * HT;                            // [NW]
-    int *wcnt = reinterpret_cast<int *>(red_t + NW);                // [NW]
+    constexpr int NH = sizeof(frag_t) / 16;
+    constexpr uint32_t CB = 32 * Elem<DT>::bytes;  // bytes of one 32-element chunk of a row
+    frag_t a0[MY], a1[MY], b0[HT], b1[HT];
+    auto load_a = [&](frag_t(&a)[MY], int c) {
+#pragma unroll
+        for (int l = 0; l < MY; ++l) a[l] = buf_load_frag<DT>(pool, off[l] + (uint32_t)c * CB);
+    };
+    auto load_b = [&](frag_t(&bq)[HT], int c) {
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) bq[ht] = q_frag<DT, HT>(qb, RS, ht, c, lane);
+    };
+    auto mma = [&](const frag_t(&a)[MY], const frag_t(&bq)[HT]) {
+#pragma unroll
+        for (int l = 0; l < MY; ++l)
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) acc[l][ht] = mfma_frag<DT>(a[l], bq[ht], acc[l][ht]);
+    };
+    const int c0 = nch & 1;  // an odd chunk count runs its first chunk unpipelined
+    if (c0) {
+        load_a(a0, 0);
+        load_b(b0, 0);
+        mma(a0, b0);
+    }
+    if (c0 >= nch) return;
+    load_a(a0, c0);
+    load_b(b0, c0);
+    int c = c0;
+    for (; c + 2 < nch; c += 2) {  // steady state: no branches between loads and MFMAs
+        load_a(a1, c + 1);
+        load_b(b1, c + 1);
+        mma(a0, b0);
+        load_a(a0, c + 2);
+        load_b(b0, c + 2);
+        mma(a1, b1);
+    }
+    load_a(a1, c + 1);  // last pair
+    load_b(b1, c + 1);
+    mma(a0, b0);
+    mma(a1, b1);
+}
 
-    // Latest tokens have the most valid slots: start them first.
-    const int64_t bt = (int64_t)gridDim.x - 1 - blockIdx.x;
-    const int b = (int)(bt / S);
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int32_t *idr = idx + bt * K;
-    float *Tr = target + bt * K;
+template <int DT, int HT, int KT, int MY = KT>
+__device__ __forceinline__ void score_dispatch(int my, f32x4 (&acc)[KT][HT], const unsigned char *__restrict__ qb, int RS,
+                                               rsrc_t pool, const uint32_t (&off)[KT], int nch, int lane) {
+    if (my == MY) {
+        score_tiles<DT, HT, MY, KT>(acc, qb, RS, pool, off, nch, lane);
+    } else if constexpr (MY > 1) {
+        score_dispatch<DT, HT, KT, MY - 1>(my, acc, qb, RS, pool, off, nch, lane);
+    }
+}
 
-    // 1. Stable compaction of the valid slots; invalid slots get target 0 here.
+// Cooperative staging of a token's queries straight from HBM into LDS: each instruction
+// moves up to 1 KB of one head row (fully coalesced); heads >= H read as zero.  The loads
+// complete asynchronously (vmcnt); wait before reading.
+template <int DT, int HT, int NW>
+__device__ __forceinline__ void stage_queries(const void *q, int64_t bt, int H, int D, unsigned char *qb, int w,
+                                              int lane) {
+    constexpr int EB = Elem<DT>::bytes;
+    const int RS = qrow_stride(D, EB), rowb = D * EB;
+    const int npiece = (rowb + 1023) >> 10;
+    const rsrc_t qr = make_rsrc(reinterpret_cast<const char *>(q) + (size_t)bt * H * D * EB, (uint32_t)(H * D * EB));
+    for (int u = w; u < 16 * HT * npiece; u += NW) {
+        const int h = u / npiece, o = (u - h * npiece) << 10;
+        if (o + 16 * lane < rowb) {
+            const uint32_t voff = h < H ? (uint32_t)(h * rowb + o + 16 * lane) : 0x80000000u;
+            buf_load_lds16(qr, qb + h * RS + o, voff);
+        }
+    }
+}
+
+// Stable compaction of the valid slots of a row (slot order kept) by the whole workgroup,
+// one barrier.  Invalid slots get target 0 here.  Returns the valid count (uniform).
+template <int NW, int KP>
+__device__ __forceinline__ int compact_slots(const int32_t *idr, int K, int N, float *Tr, int32_t *crow,
+                                             int32_t *cslot, int *wcnt, int tid, int w, int lane) {
+    int v[KP];
+    bool ok[KP];
+    int pre[KP];
+#pragma unroll
+    for (int pss = 0; pss < KP; ++pss) {
+        const int k = pss * NW * 64 + tid;
+        v[pss] = k < K ? idr[k] : -1;
+    }
+#pragma unroll
+    for (int pss = 0; pss < KP; ++pss) {
+        const int k = pss * NW * 64 + tid;
+        ok[pss] = k < K && v[pss] >= 0 && v[pss] < N;
+        if (k < K && !ok[pss]) Tr[k] = 0.f;
+        const uint64_t bal = __ballot(ok[pss]);
+        pre[pss] = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        if (lane == 0) wcnt[pss * NW + w] = __popcll(bal);
+    }
+    __syncthreads();
     int base = 0;
-    for (int k0 = 0; k0 < K; k0 += NW * 64) {
-        const int k = k0 + tid;
-        const int v = k < K ? idr[k] : -1;
-        const bool ok = k < K && v >= 0 && v < N;
-        if (k < K && !ok) Tr[k] = 0.f;
-        const uint64_t bal = __ballot(ok);
-        const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-        if (lane == 0) wcnt[w] = __popcll(bal);
-        __syncthreads();
+#pragma unroll
+    for (int pss = 0; pss < KP; ++pss) {
         int off = base, tot = 0;
         for (int i = 0; i < NW; ++i) {
-            const int c = wcnt[i];
+            const int c = wcnt[pss * NW + i];
             off += i < w ? c : 0;
             tot += c;
         }
-        if (ok) {
-            crow[off + pre] = v;
-            cslot[off + pre] = k;
+        if (ok[pss]) {
+            crow[off + pre[pss]] = v[pss];
+            cslot[off + pre[pss]] = pss * NW * 64 + tid;
         }
         base += tot;
-        __syncthreads();
     }
-    const int nvalid = base;
-    if (nvalid == 0) return;  // empty row: already all zeros
+    return base;
+}
 
-    // 2. Stage the token's queries (all heads; padded heads are zero) in fragment order.
-    {
-        const size_t qrow = (size_t)bt * H * D;
-        const int upr = D >> 3;
-        for (int u = tid; u < 16 * HT * upr; u += NW * 64) {
-            const int h = u / upr, cu = u - h * upr;
-            qs[((h >> 4) * nch + (cu >> 2)) * 64 + (h & 15) + 16 * (cu & 3)] =
-                h < H ? load_frag<DT>(q, qrow + (size_t)h * D + 8 * cu) : zero_frag<DT>();
-        }
-    }
-    __syncthreads();
+// One workgroup per token (latest tokens first, they hold the most valid slots).
+template <int DT, int HT, int KT, int NW>
+__global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kernel(
+    const void *__restrict__ q, const void *__restrict__ pool, const int32_t *__restrict__ idx,
+    const float *__restrict__ nc_lse, int S, int H, int D, int N, int K, float scale_log2, float l1_floor,
+    float *__restrict__ target) {
+    constexpr int EB = Elem<DT>::bytes;
+    constexpr int KP = 2;  // slot passes of NW*64 (K <= 2*NW*64)
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int nch = D >> 5;
+    const int RS = qrow_stride(D, EB);
+    unsigned char *qb = smem;                                                  // [16*HT rows][RS bytes]
+    int32_t *crow = reinterpret_cast<int32_t *>(smem + 16 * HT * RS);         // [K] pool row per compacted slot
+    int32_t *cslot = crow + K;                                                // [K] slot index per compacted slot
+    float *red_m = reinterpret_cast<float *>(cslot + K);                      // [NW][16*HT] per-wave head max
+    float *red_s = red_m + NW * 16 * HT;                                      // [NW][16*HT] per-wave head sum
+    float *red_t = red_s + NW * 16 * HT;                                      // [NW] per-wave row mass
+    int *wcnt = reinterpret_cast<int *>(red_t + NW);                          // [KP][NW] valid-slot counts
 
-    // 3. Scores of this wave's slot tiles: tiles w, w+NW, w+2NW, ... of the compacted list.
-    const int ntiles = (nvalid + 15) >> 4;
+    const int64_t bt = (int64_t)gridDim.x - 1 - blockIdx.x;
+    const int b = (int)(bt / S);
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    float *Tr = target + bt * K;
+
+    // 0./1. Query staging (asynchronous) overlaps the slot compaction.
+    stage_queries<DT, HT, NW>(q, bt, H, D, qb, w, lane);
+    const int nv = compact_slots<NW, KP>(idx + bt * K, K, N, Tr, crow, cslot, wcnt, tid, w, lane);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's query loads have landed in LDS
+    __syncthreads();                // ... and everyone else's; the compacted list is complete
+    if (nv == 0) return;            // empty row: already all zeros
+
+    // 2. Scores of this wave's slot tiles: tiles w, w+NW, w+2NW, ... of the compacted list.
+    const int ntiles = (nv + 15) >> 4;
     const int my = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;
-    size_t off[KT];
-#pragma unroll
-    for (int l = 0; l < KT; ++l) {
-        const int pos = 16 * (w + l * NW) + (lane & 15);
-        const int r = (l < my && pos < nvalid) ? crow[pos] : crow[0];
-        off[l] = ((size_t)b * N + r) * D + 8 * (lane >> 4);
-    }
+    const rsrc_t pr = make_rsrc(reinterpret_cast<const char *>(pool) + (size_t)b * N * D * EB,
+                                (uint32_t)((size_t)N * D * EB));
     f32x4 acc[KT][HT];
 #pragma unroll
     for (int l = 0; l < KT; ++l)
 #pragma unroll
         for (int h = 0; h < HT; ++h) acc[l][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int c = 0; c < nch; ++c) {
-        frag_t bq[HT];
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) bq[ht] = qs[(ht * nch + c) * 64 + lane];
+    {
+        uint32_t off[KT];
 #pragma unroll
         for (int l = 0; l < KT; ++l) {
-            if (l < my) {
-                const frag_t a = load_frag<DT>(pool, off[l] + 32 * c);
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht) acc[l][ht] = mfma_frag<DT>(a, bq[ht], acc[l][ht]);
-            }
+            const int pos = 16 * (w + l * NW) + (lane & 15);
+            const int r = (l < my && pos < nv) ? crow[pos] : crow[0];
+            off[l] = (uint32_t)((r * D + 8 * (lane >> 4)) * EB);
         }
+        if (my > 0) score_dispatch<DT, HT, KT>(my, acc, qb, RS, pr, off, nch, lane);
     }
 
-    // 4. Per-head maximum over the row's valid slots (log2 domain).
+    // 3. Per-head maximum and sum of exp2 over this wave's valid slots (log2 domain).
     const int prow = 4 * (lane >> 4);
-    float mx[HT];
+    float mloc[HT], sloc[HT];
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) mx[ht] = -INFINITY;
+    for (int ht = 0; ht < HT; ++ht) mloc[ht] = -INFINITY;
 #pragma unroll
     for (int l = 0; l < KT; ++l)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bool ok = l < my && 16 * (w + l * NW) + prow + i < nvalid;
+            const bool ok = l < my && 16 * (w + l * NW) + prow + i < nv;
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
                 const float x = ok ? acc[l][ht][i] * scale_log2 : -INFINITY;
                 acc[l][ht][i] = x;
-                mx[ht] = fmaxf(mx[ht], x);
+                mloc[ht] = fmaxf(mloc[ht], x);
             }
         }
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-        mx[ht] = cols4_max(mx[ht]);
-        if (lane < 16) red_a[w * 16 * HT + ht * 16 + lane] = mx[ht];
+        mloc[ht] = cols4_max(mloc[ht]);
+        sloc[ht] = 0.f;
     }
-    __syncthreads();
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        float m = -INFINITY;
-        for (int i = 0; i < NW; ++i) m = fmaxf(m, red_a[i * 16 * HT + ht * 16 + (lane & 15)]);
-        mx[ht] = m;
-    }
-
-    // 5. Per-head sum of exp2(c - max); keep the exponentials in the accumulators.
-    float sm[HT];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) sm[ht] = 0.f;
 #pragma unroll
     for (int l = 0; l < KT; ++l)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
-                const float e = fast_exp2(acc[l][ht][i] - mx[ht]);
+                const float x = acc[l][ht][i];
+                const float e = x == -INFINITY ? 0.f : fast_exp2(x - mloc[ht]);
                 acc[l][ht][i] = e;
-                sm[ht] += e;
+                sloc[ht] += e;
             }
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-        sm[ht] = cols4_sum(sm[ht]);
-        if (lane < 16) red_b[w * 16 * HT + ht * 16 + lane] = sm[ht];
+        sloc[ht] = cols4_sum(sloc[ht]);
+        if (lane < 16) {
+            red_m[w * 16 * HT + ht * 16 + lane] = mloc[ht];
+            red_s[w * 16 * HT + ht * 16 + lane] = sloc[ht];
+        }
     }
     __syncthreads();
 
-    // Joint denominator: full_h = log(sum_k exp(c_hk) + exp(nc_lse_h)); a head's weight
-    // on the compressed part is exp(c_max_h - full_h) times its exp2(c - c_max) values.
+    // 4. Joint denominator per head: full_h = log(sum_k exp(c_hk) + exp(nc_lse_h)); this
+    //    wave's exp2(c - mloc) values carry weight exp2(mloc - full) in p.
     float wgt[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         const int h = ht * 16 + (lane & 15);
-        float s = 0.f;
-        for (int i = 0; i < NW; ++i) s += red_b[i * 16 * HT + ht * 16 + (lane & 15)];
-        const float clse = mx[ht] + fast_log2(s);
+        float M = -INFINITY;
+        for (int i = 0; i < NW; ++i) M = fmaxf(M, red_m[i * 16 * HT + ht * 16 + (lane & 15)]);
+        float ssum = 0.f;
+        for (int i = 0; i < NW; ++i) {
+            const float mi = red_m[i * 16 * HT + ht * 16 + (lane & 15)];
+            ssum += mi == -INFINITY ? 0.f : red_s[i * 16 * HT + ht * 16 + (lane & 15)] * fast_exp2(mi - M);
+        }
+        const float clse = M + fast_log2(ssum);
         float full = clse;
         if (nc_lse != nullptr && h < H) full = logaddexp2(clse, nc_lse[bt * H + h] * kLog2e);
-        wgt[ht] = h < H ? fast_exp2(mx[ht] - full) : 0.f;
+        wgt[ht] = (h < H && mloc[ht] != -INFINITY) ? fast_exp2(mloc[ht] - full) : 0.f;
     }
 
-    // 6. Head sum m_k (16-lane row reduction) and the row total.
+    // 5. Head sum m_k (16-lane row reduction) and the row total.
     float m[KT][4];
     float part = 0.f;
 #pragma unroll
     for (int l = 0; l < KT; ++l)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float v = 0.f;
+            float sum = 0.f;
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) v += acc[l][ht][i] * wgt[ht];
-            v = row16_sum(v);
-            m[l][i] = v;
-            part += v;  // invalid slots hold exactly 0
+            for (int ht = 0; ht < HT; ++ht) sum += acc[l][ht][i] * wgt[ht];
+            sum = row16_sum(sum);
+            m[l][i] = sum;
+            part += sum;  // invalid slots hold exactly 0
         }
     part = cols4_sum(part);
     if (lane == 0) red_t[w] = part;
@@ -206,15 +301,15 @@ __global__ __launch_bounds__(NW * 64) void distill_target_kernel(
     for (int i = 0; i < NW; ++i) tot += red_t[i];
     const float den = fmaxf(tot, l1_floor);
 
-    // 7. Scatter the row back to slot order.
+    // 6. Scatter the row back to slot order.
     const int isel = lane & 15;
     if (isel < 4) {
 #pragma unroll
         for (int l = 0; l < KT; ++l) {
             const int pos = 16 * (w + l * NW) + prow + isel;
-            if (l < my && pos < nvalid) {
-                const float v = isel == 0 ? m[l][0] : isel == 1 ? m[l][1] : isel == 2 ? m[l][2] : m[l][3];
-                Tr[cslot[pos]] = v / den;
+            if (l < my && pos < nv) {
+                const float val = isel == 0 ? m[l][0] : isel == 1 ? m[l][1] : isel == 2 ? m[l][2] : m[l][3];
+                Tr[cslot[pos]] = val / den;
             }
         }
     }
@@ -223,16 +318,18 @@ __global__ __launch_bounds__(NW * 64) void distill_target_kernel(
 template <int DT, int HT, int KT, int NW>
 hipError_t launch3(const void *q, const void *pool, const int32_t *idx, const float *nc_lse, int B, int S, int H,
                    int D, int N, int K, float scale, float l1_floor, float *target, hipStream_t stream) {
-    const size_t lds = (size_t)HT * (D / 32) * 64 * sizeof(typename Elem<DT>::frag_t) + (size_t)2 * K * 4 +
-                       (size_t)2 * NW * 16 * HT * 4 + (size_t)NW * 8;
+    const size_t lds = (size_t)16 * HT * (D * Elem<DT>::bytes + 16) + (size_t)8 * K + (size_t)2 * NW * 16 * HT * 4 +
+                       (size_t)NW * 4 + (size_t)2 * NW * 4;
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
     const float fl = l1_floor > 0.f ? l1_floor : FLT_MIN;
+    auto kfn = &distill_target_kernel<DT, HT, KT, NW>;
     if (lds > 65536) {  // opt in to more than 64 KiB of LDS per workgroup (gfx950 has 160 KiB per CU)
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&distill_target_kernel<DT, HT, KT, NW>),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kfn),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((distill_target_kernel<DT, HT, KT, NW>), dim3((unsigned)((int64_t)B * S)), dim3(NW * 64),
-                       lds, stream, q, pool, idx, nc_lse, S, H, D, N, K, scale * kLog2e, fl, target);
+    hipLaunchKernelGGL(kfn, dim3((unsigned)((int64_t)B * S)), dim3(NW * 64), lds, stream, q, pool, idx, nc_lse, S, H,
+                       D, N, K, scale * kLog2e, fl, target);
     return hipGetLastError();
 }
 
@@ -240,12 +337,13 @@ template <int DT, int HT>
 hipError_t launch2(const void *q, const void *pool, const int32_t *idx, const float *nc_lse, int B, int S, int H,
                    int D, int N, int K, float scale, float l1_floor, float *target, hipStream_t stream) {
 #define SD_T(KT, NW) launch3<DT, HT, KT, NW>(q, pool, idx, nc_lse, B, S, H, D, N, K, scale, l1_floor, target, stream)
+    // K <= 16*NW*KT.
     if (K <= 16) return SD_T(1, 1);
     if (K <= 64) return SD_T(1, 4);
     if (K <= 128) return SD_T(2, 4);
     if (K <= 256) return SD_T(4, 4);
-    if (K <= 512) return SD_T(8, 4);
-    return SD_T(8, 8);
+    if (K <= 512) return SD_T(4, 8);
+    return SD_T(4, 16);
 #undef SD_T
 }
 

@@ -64,6 +64,80 @@ __device__ __forceinline__ f32x4 mfma_frag<1>(f32x8 a, f32x8 b, f32x4 acc) {
     return acc;
 }
 
+// ---- buffer loads ------------------------------------------------------------------
+// Raw buffer resources give 32-bit per-lane byte offsets and hardware bounds checking:
+// any access at or beyond `bytes` reads as zero.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
+// One fragment (8 elements) of a row at byte offset `byte_off`.
+template <int DT>
+__device__ __forceinline__ typename Elem<DT>::frag_t buf_load_frag(rsrc_t r, uint32_t byte_off);
+template <>
+__device__ __forceinline__ u32x4 buf_load_frag<0>(rsrc_t r, uint32_t byte_off) {
+    return buf_load16(r, byte_off);
+}
+template <>
+__device__ __forceinline__ f32x8 buf_load_frag<1>(rsrc_t r, uint32_t byte_off) {
+    const f32x4 lo = __builtin_bit_cast(f32x4, buf_load16(r, byte_off));
+    const f32x4 hi = __builtin_bit_cast(f32x4, buf_load16(r, byte_off + 16));
+    return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Direct buffer -> LDS load of 16 bytes per lane: lane l's bytes land at lds + 16*l.
+// `lds` must be wave-uniform.  Completion is tracked by vmcnt (wait before reading).
+__device__ __forceinline__ void buf_load_lds16(rsrc_t r, void *lds, uint32_t byte_off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, byte_off, 0, 0, 0);
+}
+
+// A fragment stored in LDS as NH = sizeof(frag)/16 planes of 64 lanes x 16 bytes.
+template <int DT>
+__device__ __forceinline__ typename Elem<DT>::frag_t lds_frag(const u32x4 *units, int unit);
+template <>
+__device__ __forceinline__ u32x4 lds_frag<0>(const u32x4 *units, int unit) {
+    return units[unit];
+}
+template <>
+__device__ __forceinline__ f32x8 lds_frag<1>(const u32x4 *units, int unit) {
+    const f32x4 lo = __builtin_bit_cast(f32x4, units[unit]);
+    const f32x4 hi = __builtin_bit_cast(f32x4, units[unit + 64]);
+    return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// ---- coalesced gather of 16-row operand tiles (bf16) ------------------------------
+// A 16x16x32 operand tile puts 4 lanes on each row (64 bytes of a row per load), which
+// costs one 128-byte L2 request per row and half-uses it.  Instead, the two chunks of a
+// 128-byte line (chunks 2p and 2p+1) of a 16-row tile are fetched with two loads that
+// each cover 8 rows x 128 bytes:
+//     load lo: lane (r = l/16, x = l%16) holds row x%8,     16-byte segment r + 4*(x/8)
+//     load hi: lane (r, x)               holds row 8 + x%8, segment r + 4*(x/8)
+// The fragment of chunk 2p (segments 0..3) is lo for x < 8 and hi rotated by 8 lanes
+// within the 16-lane row for x >= 8; chunk 2p+1 (segments 4..7) is lo rotated by 8 for
+// x < 8 and hi for x >= 8.  Byte offset of a lane's segment inside the line:
+__device__ __forceinline__ uint32_t pair_seg_bytes(int lane) { return (uint32_t)(16 * ((lane >> 4) + 4 * ((lane >> 3) & 1))); }
+
+__device__ __forceinline__ uint32_t ror8(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);  // row_ror:8
+}
+
+// In place: lo becomes the fragment of chunk 2p, hi the fragment of chunk 2p+1.
+__device__ __forceinline__ void pair_to_frags(u32x4 &lo, u32x4 &hi, bool low_half) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const uint32_t rl = ror8(lo[v]), rh = ror8(hi[v]);
+        lo[v] = low_half ? lo[v] : rh;
+        hi[v] = low_half ? rl : hi[v];
+    }
+}
+
 // ---- cross-lane reductions -------------------------------------------------------
 // Sum over the 16 lanes of a DPP row (lanes sharing l/16); every lane gets the total.
 __device__ __forceinline__ float row16_sum(float v) {

@@ -15,6 +15,8 @@
 // so a lane ends up holding one head column and 4 keys per tile; the masked online
 // maximum and sum over keys therefore stay in registers and only need two cross-lane
 // steps.  The queries are the only HBM stream; everything else is reused from L2/LDS.
+#include <algorithm>
+
 #include "sd_device.hpp"
 #include "sd_internal.hpp"
 
@@ -145,6 +147,195 @@ __global__ __launch_bounds__(kWinTok * 64) void window_lse_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------------
+// bf16 fast path (D % 64 == 0).  A workgroup owns TOK = 4 consecutive tokens x HG head
+// tiles (one 16-head tile per wave: 4 x 4 = 16 waves at H = 64); wave w handles token
+// w / HG and head tile w % HG.  D is walked in stages of 64 elements (128 bytes of every
+// row).  Per stage the workgroup stages, with direct loads into LDS that each move 8
+// rows x 128 bytes (fully coalesced):
+//   * the key band its tokens span (16-key tiles covering [t0-W+1, t0+3]; from L2),
+//     double buffered, one stage ahead;
+//   * the queries of its 4 tokens (from HBM), triple buffered, two stages ahead.
+// Rows are stored with their 16-byte segments XOR-swizzled by (row >> 1) & 7, so the
+// 16-row MFMA fragment reads hit distinct LDS banks.  Loads retire in order, so each
+// stage ends with a counted wait that leaves only the farthest query stage in flight.
+// Every wave computes the same NBT tiles from its first window tile; keys outside the
+// token's window are masked, so the loop has no branches.
+constexpr int kTokMfma = 4;
+
+__device__ __forceinline__ uint32_t sw_pos(int r, int x) {  // byte offset of row r, segment x
+    return (uint32_t)(r * 128 + ((x ^ ((r >> 1) & 7)) << 4));
+}
+
+template <int NBT>
+__global__ __launch_bounds__(1024) void window_lse_mfma_kernel(
+    const void *__restrict__ q, const void *__restrict__ kwin, const float *__restrict__ sink,
+    const int32_t *__restrict__ seg, int S, int H, int D, int W, int HG, int nballoc, float scale_log2,
+    float *__restrict__ nc_lse) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int b = blockIdx.y;
+    const int t0 = blockIdx.x * kTokMfma;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int nwaves = blockDim.x >> 6;
+    const int tok = w / HG, hg = w - tok * HG;
+    const int t = t0 + tok;
+    const bool active = t < S;
+    const int HP = HG * 16;  // padded head count
+
+    const int tlast = min(t0 + kTokMfma - 1, S - 1);
+    const int tile0 = max(t0 - W + 1, 0) >> 4;
+    const int nb = (tlast >> 4) - tile0 + 1;  // band tiles actually loaded
+    const int band_bytes = nballoc * 16 * 128;
+    const int qst_bytes = kTokMfma * HP * 128;
+    unsigned char *band = smem;                   // [2][nballoc*16 rows][128 B]
+    unsigned char *qst = smem + 2 * band_bytes;   // [3][TOK*HP rows][128 B]
+    int32_t *segband = reinterpret_cast<int32_t *>(qst + 3 * qst_bytes);  // [nballoc*16]
+
+    const rsrc_t kr = make_rsrc(reinterpret_cast<const char *>(kwin) + (size_t)b * S * D * 2, (uint32_t)((size_t)S * D * 2));
+    const int nqtok = min(kTokMfma, S - t0);
+    const rsrc_t qr = make_rsrc(reinterpret_cast<const char *>(q) + ((size_t)b * S + t0) * H * D * 2,
+                                (uint32_t)(nqtok * H * D * 2));
+    const int r_in = lane >> 3;
+    // Key band of D stage st into band buffer st&1; instruction m covers band rows 8m..8m+7.
+    auto stage_band = [&](int st) {
+        unsigned char *dst = band + (st & 1) * band_bytes;
+        for (int m = w; m < 2 * nb; m += nwaves) {
+            const int r = 8 * m + r_in;
+            const int x = (lane & 7) ^ ((r >> 1) & 7);  // lands at segment lane&7 of the swizzled row
+            const int key = tile0 * 16 + r;
+            const uint32_t voff = key < S ? (uint32_t)((key * D + st * 64 + 8 * x) * 2) : 0x80000000u;
+            buf_load_lds16(kr, dst + m * 1024, voff);
+        }
+    };
+    // Queries of D stage st into query buffer st%3; row = tok*HP + head.
+    auto stage_q = [&](int st) {
+        unsigned char *dst = qst + (st % 3) * qst_bytes;
+        for (int m = w; m < kTokMfma * HP / 8; m += nwaves) {
+            const int r = 8 * m + r_in;
+            const int x = (lane & 7) ^ ((r >> 1) & 7);
+            const int tk = r / HP, hd = r - tk * HP;
+            const uint32_t voff = hd < H ? (uint32_t)(((tk * H + hd) * D + st * 64 + 8 * x) * 2) : 0x80000000u;
+            buf_load_lds16(qr, dst + m * 1024, voff);
+        }
+    };
+    if (seg) {
+        for (int i = tid; i < nb * 16; i += blockDim.x) {
+            const int key = tile0 * 16 + i;
+            segband[i] = key < S ? seg[(size_t)b * S + key] : INT32_MIN;
+        }
+    }
+    const int seg_t = (seg && active) ? seg[(size_t)b * S + t] : 0;
+
+    // This wave's first window tile inside the band.
+    const int kf = max(t - W + 1, 0);
+    const int wfirst = active ? (kf >> 4) - tile0 : 0;
+
+    f32x4 acc[NBT];
+#pragma unroll
+    for (int j = 0; j < NBT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // The swizzle only depends on the row within a 16-row tile, so tile j's fragment sits
+    // at a fixed base plus 2048*j bytes (an immediate offset).
+    const int rq = tok * HP + hg * 16 + (lane & 15);
+    const int rb = wfirst * 16 + (lane & 15);
+    auto compute = [&](int st) {
+        const unsigned char *bsrc = band + (st & 1) * band_bytes;
+        const unsigned char *qsrc = qst + (st % 3) * qst_bytes;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int x = 4 * c + (lane >> 4);
+            const u32x4 bq = *reinterpret_cast<const u32x4 *>(qsrc + sw_pos(rq, x));
+            const unsigned char *fb = bsrc + sw_pos(rb, x);
+            u32x4 a = *reinterpret_cast<const u32x4 *>(fb);
+#pragma unroll
+            for (int j = 0; j < NBT; ++j) {
+                u32x4 an = a;
+                if (j + 1 < NBT) an = *reinterpret_cast<const u32x4 *>(fb + 2048 * (j + 1));
+                acc[j] = mfma_frag<0>(a, bq, acc[j]);
+                a = an;
+            }
+        }
+    };
+
+    const int nst = D >> 6;
+    // my far query loads per stage (the wave's share of the TOK*HP/8 instructions)
+    const int nfar = (kTokMfma * HP / 8 - w + nwaves - 1) / nwaves;
+    stage_q(0);
+    if (nst > 1) stage_q(1);
+    stage_band(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+        if (st + 1 < nst) stage_band(st + 1);
+        const bool far = st + 2 < nst;
+        if (far) stage_q(st + 2);
+        compute(st);
+        if (far && nfar > 0) {
+            // wait for everything but this wave's nfar (<= 2) far query loads
+            if (nfar == 1) __builtin_amdgcn_s_waitcnt((1 & 0xF) | (0x7 << 4) | (0xF << 8));
+            else __builtin_amdgcn_s_waitcnt((2 & 0xF) | (0x7 << 4) | (0xF << 8));
+        } else {
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+        __syncthreads();
+    }
+    if (!active) return;
+
+    // Masked log-sum-exp over the window keys (log2 domain), then the sink.
+    const int kbase = 16 * (tile0 + wfirst) + 4 * (lane >> 4);
+    const int lo = t - W + 1;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NBT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = kbase + 16 * j + i;
+            bool ok = key >= lo && key <= t;
+            if (seg && ok) ok = segband[key - 16 * tile0] == seg_t;
+            const float x = ok ? acc[j][i] * scale_log2 : -INFINITY;
+            acc[j][i] = x;
+            mx = fmaxf(mx, x);
+        }
+    mx = cols4_max(mx);
+    float sm = 0.f;
+#pragma unroll
+    for (int j = 0; j < NBT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm += fast_exp2(acc[j][i] - mx);
+    sm = cols4_sum(sm);
+    const int head = hg * 16 + (lane & 15);
+    float lse2 = mx + fast_log2(sm);
+    if (sink && head < H) lse2 = logaddexp2(lse2, sink[head] * kLog2e);
+    if (lane < 16 && head < H) nc_lse[((size_t)b * S + t) * H + head] = lse2 * kLn2;
+}
+
+template <int NBT>
+hipError_t launch_mfma(const void *q, const void *kwin, const float *sink, const int32_t *seg, int B, int S, int H,
+                       int D, int W, float scale, float *nc_lse, hipStream_t stream) {
+    const int HG = (H + 15) / 16;
+    const int nballoc = std::max(win_tiles(W + kTokMfma - 1), NBT + 1);
+    const size_t lds = (size_t)2 * nballoc * 16 * 128 + (size_t)3 * kTokMfma * HG * 16 * 128 + (size_t)nballoc * 16 * 4;
+    auto kfn = &window_lse_mfma_kernel<NBT>;
+    if (lds > 65536) {  // opt in to more than 64 KiB of LDS per workgroup (gfx950 has 160 KiB per CU)
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kfn),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    dim3 grid((S + kTokMfma - 1) / kTokMfma, B);
+    hipLaunchKernelGGL(kfn, grid, dim3(kTokMfma * HG * 64), lds, stream, q, kwin, sink, seg, S, H, D, W, HG, nballoc,
+                       scale * kLog2e, nc_lse);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_w(const void *q, const void *kwin, const float *sink, const int32_t *seg, int B, int S, int H,
+                         int D, int W, float scale, float *nc_lse, hipStream_t stream) {
+    const int nt = win_tiles(W);
+    if (nt <= 2) return launch_mfma<2>(q, kwin, sink, seg, B, S, H, D, W, scale, nc_lse, stream);
+    if (nt <= 3) return launch_mfma<3>(q, kwin, sink, seg, B, S, H, D, W, scale, nc_lse, stream);
+    if (nt <= 5) return launch_mfma<5>(q, kwin, sink, seg, B, S, H, D, W, scale, nc_lse, stream);
+    return launch_mfma<9>(q, kwin, sink, seg, B, S, H, D, W, scale, nc_lse, stream);
+}
+
 template <int DT, int HT, int NBT>
 hipError_t launch3(const void *q, const void *kwin, const float *sink, const int32_t *seg, int B, int S, int H,
                    int D, int W, float scale, float *nc_lse, hipStream_t stream) {
@@ -180,6 +371,8 @@ hipError_t launch1(const void *q, const void *kwin, const float *sink, const int
 hipError_t launch_window_lse(const void *q, const void *kwin, const float *sink, const int32_t *seg, int B,
                              int S, int H, int D, int W, float scale, int dtype, float *nc_lse,
                              hipStream_t stream) {
+    if (dtype == 0 && D % 64 == 0)  // bf16 fast path: 4 tokens x up to 4 head tiles per workgroup
+        return launch_mfma_w(q, kwin, sink, seg, B, S, H, D, W, scale, nc_lse, stream);
     if (dtype == 0) return launch1<0>(q, kwin, sink, seg, B, S, H, D, W, scale, nc_lse, stream);
     return launch1<1>(q, kwin, sink, seg, B, S, H, D, W, scale, nc_lse, stream);
 }

@@ -95,9 +95,11 @@ int window_lse(const void *q, const void *kwin, const float *sink, const int32_t
  *   idx    [B,S,K]   int32            top-k pool rows; invalid slots as above
  *   nc_lse [B,S,H]   float32 or NULL  from window_lse; NULL = legacy per-branch target
  *                                     (each head renormalised over its compressed part)
+ *   scale            softmax scale, positive and finite (1/sqrt(D) for the method)
  *   l1_floor         <= 0 selects FLT_MIN (2^-126); 1e-10 reproduces the legacy floor
  *   target [B,S,K]   float32 out      a row with no valid slot is all zeros
- * Limits: D % 32 == 0, D <= 512; H <= 64; K <= 1024.
+ * Limits: D % 32 == 0, D <= 512; H <= 64; K <= 1024.  A non-positive or non-finite
+ * scale is rejected with SD_ERR_BAD_SHAPE.
  */
 int distill_target(const void *q, const void *pool, const int32_t *idx, const float *nc_lse,
                    int B, int S, int H, int D, int N, int K, float scale, float l1_floor,

@@ -79,8 +79,8 @@ int distill_target(const void *q, const void *pool, const int32_t *idx, const fl
     if (st != SD_OK) return st;
     if (N <= 0 || K <= 0) return fail(SD_ERR_BAD_SHAPE, "distill_target: N=%d and K=%d must be positive", N, K);
     if (K > sd::kMaxTopK) return fail(SD_ERR_UNSUPPORTED, "distill_target: K=%d exceeds %d", K, sd::kMaxTopK);
-    if (!isfinite(scale) || isnan(l1_floor))
-        return fail(SD_ERR_BAD_SHAPE, "distill_target: scale must be finite and l1_floor not NaN");
+    if (!isfinite(scale) || !(scale > 0.f) || isnan(l1_floor))
+        return fail(SD_ERR_BAD_SHAPE, "distill_target: scale must be positive and finite, l1_floor not NaN");
     return hip_status(sd::launch_distill_target(q, pool, idx, nc_lse, B, S, H, D, N, K, scale, l1_floor, dtype,
                                                 target, stream),
                       "distill_target launch");

@@ -55,7 +55,6 @@ template <int DT, int HT, int MY, int KT>
 __device__ __forceinline__ void score_tiles(f32x4 (&acc)[KT][HT], const unsigned char *__restrict__ qb, int RS, rsrc_t pool,
                                             const uint32_t (&off)[KT], int nch, int lane) {
     using frag_t = typename Elem<DT>::frag_t;
-    constexpr int NH = sizeof(frag_t) / 16;
     constexpr uint32_t CB = 32 * Elem<DT>::bytes;  // bytes of one 32-element chunk of a row
     frag_t a0[MY], a1[MY], b0[HT], b1[HT];
     auto load_a = [&](frag_t(&a)[MY], int c) {
@@ -187,7 +186,7 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
 
     const int64_t bt = (int64_t)gridDim.x - 1 - blockIdx.x;
     const int b = (int)(bt / S);
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     float *Tr = target + bt * K;
 
     // 0./1. Query staging (asynchronous) overlaps the slot compaction.
@@ -202,11 +201,15 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
     const int my = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;
     const rsrc_t pr = make_rsrc(reinterpret_cast<const char *>(pool) + (size_t)b * N * D * EB,
                                 (uint32_t)((size_t)N * D * EB));
+    // Tiles this wave does not compute stay at -inf: they drop out of the maximum and
+    // their exponentials are exactly 0, so the epilogue needs no per-element masks.
     f32x4 acc[KT][HT];
 #pragma unroll
-    for (int l = 0; l < KT; ++l)
+    for (int l = 0; l < KT; ++l) {
+        const float init = l < my ? 0.f : -INFINITY;
 #pragma unroll
-        for (int h = 0; h < HT; ++h) acc[l][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < HT; ++h) acc[l][h] = f32x4{init, init, init, init};
+    }
     {
         uint32_t off[KT];
 #pragma unroll
@@ -218,66 +221,84 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
         if (my > 0) score_dispatch<DT, HT, KT>(my, acc, qb, RS, pr, off, nch, lane);
     }
 
-    // 3. Per-head maximum and sum of exp2 over this wave's valid slots (log2 domain).
+    // 3. Per-head maximum and sum of exp2 over this wave's slots (log2 domain, scale > 0).
+    //    Padding rows of a partial last tile were scored against a valid selected row
+    //    (crow[0]), so they repeat a real score and leave the maximum exact; only their
+    //    exponentials are zeroed below.
     const int prow = 4 * (lane >> 4);
+    const int x = lane & 15, g = lane >> 4;
     float mloc[HT], sloc[HT];
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) mloc[ht] = -INFINITY;
-#pragma unroll
-    for (int l = 0; l < KT; ++l)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool ok = l < my && 16 * (w + l * NW) + prow + i < nv;
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                const float x = ok ? acc[l][ht][i] * scale_log2 : -INFINITY;
-                acc[l][ht][i] = x;
-                mloc[ht] = fmaxf(mloc[ht], x);
-            }
-        }
-#pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-        mloc[ht] = cols4_max(mloc[ht]);
-        sloc[ht] = 0.f;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int l = 0; l < KT; ++l) mx = fmaxf(mx, fmaxf(fmaxf(acc[l][ht][0], acc[l][ht][1]), fmaxf(acc[l][ht][2], acc[l][ht][3])));
+        mloc[ht] = cols4_max(mx) * scale_log2;  // -inf for a wave without tiles
     }
 #pragma unroll
-    for (int l = 0; l < KT; ++l)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                const float x = acc[l][ht][i];
-                const float e = x == -INFINITY ? 0.f : fast_exp2(x - mloc[ht]);
-                acc[l][ht][i] = e;
-                sloc[ht] += e;
-            }
-#pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-        sloc[ht] = cols4_sum(sloc[ht]);
-        if (lane < 16) {
-            red_m[w * 16 * HT + ht * 16 + lane] = mloc[ht];
-            red_s[w * 16 * HT + ht * 16 + lane] = sloc[ht];
+        const float nm = mloc[ht] == -INFINITY ? 0.f : -mloc[ht];
+        float sum = 0.f;
+#pragma unroll
+        for (int l = 0; l < KT; ++l)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e = fast_exp2(fmaf(acc[l][ht][i], scale_log2, nm));
+                acc[l][ht][i] = e;
+                sum += e;
+            }
+        sloc[ht] = sum;
+    }
+#pragma unroll
+    for (int l = 0; l < KT; ++l) {
+        const int base = 16 * (w + l * NW);
+        if (l < my && base + 16 > nv) {  // the partial tile (at most one per wave)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (base + prow + i >= nv) {
+#pragma unroll
+                    for (int ht = 0; ht < HT; ++ht) {
+                        sloc[ht] -= acc[l][ht][i];
+                        acc[l][ht][i] = 0.f;
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) sloc[ht] = cols4_sum(sloc[ht]);
+    // red_m/red_s laid out [wave][head%16][head tile]: lane x < 16 writes its HT heads at once
+    if (lane < 16) {
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            red_m[(w * 16 + x) * HT + ht] = mloc[ht];
+            red_s[(w * 16 + x) * HT + ht] = sloc[ht];
         }
     }
     __syncthreads();
 
-    // 4. Joint denominator per head: full_h = log(sum_k exp(c_hk) + exp(nc_lse_h)); this
-    //    wave's exp2(c - mloc) values carry weight exp2(mloc - full) in p.
+    // 4. Joint denominator per head, full_h = log2(sum_k 2^c_hk + 2^(nc_lse_h log2 e)):
+    //    lane (g, x) reduces head 16g + x over the waves, then every lane fetches the
+    //    HT heads it holds.  This wave's exp2(c - mloc) values carry weight 2^(mloc - full).
+    float fullv;
+    {
+        const int gg = g < HT ? g : HT - 1;
+        float M = -INFINITY;
+#pragma unroll 4
+        for (int i = 0; i < NW; ++i) M = fmaxf(M, red_m[(i * 16 + x) * HT + gg]);
+        float ssum = 0.f;
+#pragma unroll 4
+        for (int i = 0; i < NW; ++i)
+            ssum = fmaf(red_s[(i * 16 + x) * HT + gg], fast_exp2(red_m[(i * 16 + x) * HT + gg] - M), ssum);
+        fullv = M + fast_log2(ssum);
+        const int h = gg * 16 + x;
+        if (nc_lse != nullptr && h < H) fullv = logaddexp2(fullv, nc_lse[bt * H + h] * kLog2e);
+    }
     float wgt[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-        const int h = ht * 16 + (lane & 15);
-        float M = -INFINITY;
-        for (int i = 0; i < NW; ++i) M = fmaxf(M, red_m[i * 16 * HT + ht * 16 + (lane & 15)]);
-        float ssum = 0.f;
-        for (int i = 0; i < NW; ++i) {
-            const float mi = red_m[i * 16 * HT + ht * 16 + (lane & 15)];
-            ssum += mi == -INFINITY ? 0.f : red_s[i * 16 * HT + ht * 16 + (lane & 15)] * fast_exp2(mi - M);
-        }
-        const float clse = M + fast_log2(ssum);
-        float full = clse;
-        if (nc_lse != nullptr && h < H) full = logaddexp2(clse, nc_lse[bt * H + h] * kLog2e);
-        wgt[ht] = (h < H && mloc[ht] != -INFINITY) ? fast_exp2(mloc[ht] - full) : 0.f;
+        const float full = __shfl(fullv, ht * 16 + x);
+        wgt[ht] = (ht * 16 + x < H && mloc[ht] != -INFINITY) ? fast_exp2(mloc[ht] - full) : 0.f;
     }
 
     // 5. Head sum m_k (16-lane row reduction) and the row total.
@@ -288,28 +309,30 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float sum = 0.f;
+            if (l < my) {
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) sum += acc[l][ht][i] * wgt[ht];
-            sum = row16_sum(sum);
+                for (int ht = 0; ht < HT; ++ht) sum = fmaf(acc[l][ht][i], wgt[ht], sum);
+                sum = row16_sum(sum);
+            }
             m[l][i] = sum;
-            part += sum;  // invalid slots hold exactly 0
+            part += sum;  // padding rows hold exactly 0
         }
     part = cols4_sum(part);
     if (lane == 0) red_t[w] = part;
     __syncthreads();
     float tot = 0.f;
+#pragma unroll 4
     for (int i = 0; i < NW; ++i) tot += red_t[i];
-    const float den = fmaxf(tot, l1_floor);
+    const float rden = 1.f / fmaxf(tot, l1_floor);
 
-    // 6. Scatter the row back to slot order.
-    const int isel = lane & 15;
-    if (isel < 4) {
+    // 6. Scatter the row back to slot order: lane (g, x < 4) stores row 4g + x of each tile.
+    if (x < 4) {
 #pragma unroll
         for (int l = 0; l < KT; ++l) {
-            const int pos = 16 * (w + l * NW) + prow + isel;
+            const int pos = 16 * (w + l * NW) + prow + x;
             if (l < my && pos < nv) {
-                const float val = isel == 0 ? m[l][0] : isel == 1 ? m[l][1] : isel == 2 ? m[l][2] : m[l][3];
-                Tr[cslot[pos]] = val / den;
+                const float val = x == 0 ? m[l][0] : x == 1 ? m[l][1] : x == 2 ? m[l][2] : m[l][3];
+                Tr[cslot[pos]] = val * rden;
             }
         }
     }

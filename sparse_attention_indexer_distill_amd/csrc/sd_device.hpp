@@ -124,11 +124,12 @@ __device__ __forceinline__ f32x8 lds_frag<1>(const u32x4 *units, int unit) {
 // x < 8 and hi for x >= 8.  Byte offset of a lane's segment inside the line:
 __device__ __forceinline__ uint32_t pair_seg_bytes(int lane) { return (uint32_t)(16 * ((lane >> 4) + 4 * ((lane >> 3) & 1))); }
 
+// In place: lo becomes the fragment of chunk 2p, hi the fragment of chunk 2p+1
+// (low_half: lane%16 < 8).  row_ror:8 never leaves the 16-lane row, so bound_ctrl
+// costs nothing and spares the move of an "old" value: two VALU ops per dword.
 __device__ __forceinline__ uint32_t ror8(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);  // row_ror:8
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, true);  // row_ror:8
 }
-
-// In place: lo becomes the fragment of chunk 2p, hi the fragment of chunk 2p+1.
 __device__ __forceinline__ void pair_to_frags(u32x4 &lo, u32x4 &hi, bool low_half) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {

@@ -85,6 +85,9 @@ def test_distill_target_rejections(lib):
     assert _tg(lib, K=0) == sd.SD_ERR_BAD_SHAPE
     assert _tg(lib, H=0) == sd.SD_ERR_BAD_SHAPE
     assert _tg(lib, floor=float("nan")) == sd.SD_ERR_BAD_SHAPE
+    assert _tg(lib, scale=0.0) == sd.SD_ERR_BAD_SHAPE
+    assert _tg(lib, scale=-0.1) == sd.SD_ERR_BAD_SHAPE
+    assert _tg(lib, scale=float("nan")) == sd.SD_ERR_BAD_SHAPE
     assert _tg(lib, dtype=-1) == sd.SD_ERR_DTYPE
     assert _tg(lib, K=1025) == sd.SD_ERR_UNSUPPORTED
     assert _tg(lib, D=16) == sd.SD_ERR_UNSUPPORTED

@@ -95,6 +95,55 @@ __device__ __forceinline__ void score_tiles(f32x4 (&acc)[KT][HT], const unsigned
     mma(a1, b1);
 }
 
+// bf16 variant with only the pool fragments double-buffered: each query fragment is read
+// from LDS right before its MFMAs (the other waves of the SIMD cover the LDS latency),
+// which frees 4*HT registers per lane -- enough to keep the widest tile set spill-free.
+template <int HT, int MY, int KT>
+__device__ __forceinline__ void score_tiles_q1(f32x4 (&acc)[KT][HT], const unsigned char *__restrict__ qb, int RS,
+                                               rsrc_t pool, const uint32_t (&off)[KT], int nch, int lane) {
+    constexpr uint32_t CB = 64;  // bytes of one 32-element bf16 chunk of a row
+    u32x4 a0[MY], a1[MY];
+    auto load_a = [&](u32x4(&a)[MY], int c) {
+#pragma unroll
+        for (int l = 0; l < MY; ++l) a[l] = buf_load16(pool, off[l] + (uint32_t)c * CB);
+    };
+    auto mma = [&](const u32x4(&a)[MY], int c) {
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            const u32x4 b = q_frag<0, HT>(qb, RS, ht, c, lane);
+#pragma unroll
+            for (int l = 0; l < MY; ++l) acc[l][ht] = mfma_frag<0>(a[l], b, acc[l][ht]);
+        }
+    };
+    const int c0 = nch & 1;  // an odd chunk count runs its first chunk unpipelined
+    if (c0) {
+        load_a(a0, 0);
+        mma(a0, 0);
+    }
+    if (c0 >= nch) return;
+    load_a(a0, c0);
+    int c = c0;
+    for (; c + 2 < nch; c += 2) {
+        load_a(a1, c + 1);
+        mma(a0, c);
+        load_a(a0, c + 2);
+        mma(a1, c + 1);
+    }
+    load_a(a1, c + 1);
+    mma(a0, c);
+    mma(a1, c + 1);
+}
+
+template <int HT, int KT, int MY = KT>
+__device__ __forceinline__ void score_dispatch_q1(int my, f32x4 (&acc)[KT][HT], const unsigned char *__restrict__ qb,
+                                                  int RS, rsrc_t pool, const uint32_t (&off)[KT], int nch, int lane) {
+    if (my == MY) {
+        score_tiles_q1<HT, MY, KT>(acc, qb, RS, pool, off, nch, lane);
+    } else if constexpr (MY > 1) {
+        score_dispatch_q1<HT, KT, MY - 1>(my, acc, qb, RS, pool, off, nch, lane);
+    }
+}
+
 template <int DT, int HT, int KT, int MY = KT>
 __device__ __forceinline__ void score_dispatch(int my, f32x4 (&acc)[KT][HT], const unsigned char *__restrict__ qb, int RS,
                                                rsrc_t pool, const uint32_t (&off)[KT], int nch, int lane) {
@@ -165,74 +214,26 @@ __device__ __forceinline__ int compact_slots(const int32_t *idr, int K, int N, f
     return base;
 }
 
-// One workgroup per token (latest tokens first, they hold the most valid slots).
-template <int DT, int HT, int KT, int NW>
-__global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kernel(
-    const void *__restrict__ q, const void *__restrict__ pool, const int32_t *__restrict__ idx,
-    const float *__restrict__ nc_lse, int S, int H, int D, int N, int K, float scale_log2, float l1_floor,
-    float *__restrict__ target) {
-    constexpr int EB = Elem<DT>::bytes;
-    constexpr int KP = 2;  // slot passes of NW*64 (K <= 2*NW*64)
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int nch = D >> 5;
-    const int RS = qrow_stride(D, EB);
-    unsigned char *qb = smem;                                                  // [16*HT rows][RS bytes]
-    int32_t *crow = reinterpret_cast<int32_t *>(smem + 16 * HT * RS);         // [K] pool row per compacted slot
-    int32_t *cslot = crow + K;                                                // [K] slot index per compacted slot
-    float *red_m = reinterpret_cast<float *>(cslot + K);                      // [NW][16*HT] per-wave head max
-    float *red_s = red_m + NW * 16 * HT;                                      // [NW][16*HT] per-wave head sum
-    float *red_t = red_s + NW * 16 * HT;                                      // [NW] per-wave row mass
-    int *wcnt = reinterpret_cast<int *>(red_t + NW);                          // [KP][NW] valid-slot counts
+// ---- epilogue of one token, shared by the kernels below ----------------------------
+// Wave w holds slot tiles w, w+NW, ... (my of them, the rest of acc at -inf); lane
+// (g, x) = (lane/16, lane%16) holds rows 4g+i of each tile for heads 16ht+x.
 
-    const int64_t bt = (int64_t)gridDim.x - 1 - blockIdx.x;
-    const int b = (int)(bt / S);
-    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    float *Tr = target + bt * K;
-
-    // 0./1. Query staging (asynchronous) overlaps the slot compaction.
-    stage_queries<DT, HT, NW>(q, bt, H, D, qb, w, lane);
-    const int nv = compact_slots<NW, KP>(idx + bt * K, K, N, Tr, crow, cslot, wcnt, tid, w, lane);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's query loads have landed in LDS
-    __syncthreads();                // ... and everyone else's; the compacted list is complete
-    if (nv == 0) return;            // empty row: already all zeros
-
-    // 2. Scores of this wave's slot tiles: tiles w, w+NW, w+2NW, ... of the compacted list.
-    const int ntiles = (nv + 15) >> 4;
-    const int my = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;
-    const rsrc_t pr = make_rsrc(reinterpret_cast<const char *>(pool) + (size_t)b * N * D * EB,
-                                (uint32_t)((size_t)N * D * EB));
-    // Tiles this wave does not compute stay at -inf: they drop out of the maximum and
-    // their exponentials are exactly 0, so the epilogue needs no per-element masks.
-    f32x4 acc[KT][HT];
-#pragma unroll
-    for (int l = 0; l < KT; ++l) {
-        const float init = l < my ? 0.f : -INFINITY;
-#pragma unroll
-        for (int h = 0; h < HT; ++h) acc[l][h] = f32x4{init, init, init, init};
-    }
-    {
-        uint32_t off[KT];
-#pragma unroll
-        for (int l = 0; l < KT; ++l) {
-            const int pos = 16 * (w + l * NW) + (lane & 15);
-            const int r = (l < my && pos < nv) ? crow[pos] : crow[0];
-            off[l] = (uint32_t)((r * D + 8 * (lane >> 4)) * EB);
-        }
-        if (my > 0) score_dispatch<DT, HT, KT>(my, acc, qb, RS, pr, off, nch, lane);
-    }
-
-    // 3. Per-head maximum and sum of exp2 over this wave's slots (log2 domain, scale > 0).
-    //    Padding rows of a partial last tile were scored against a valid selected row
-    //    (crow[0]), so they repeat a real score and leave the maximum exact; only their
-    //    exponentials are zeroed below.
-    const int prow = 4 * (lane >> 4);
-    const int x = lane & 15, g = lane >> 4;
-    float mloc[HT], sloc[HT];
+// Per-head maximum and sum of exp2 over this wave's slots (log2 domain, scale > 0),
+// published in red_m/red_s laid out [wave][head%16][head tile].  Padding rows of a
+// partial last tile were scored against a valid selected row (crow[0]), so they repeat
+// a real score and leave the maximum exact; only their exponentials are zeroed.  On
+// return acc holds exp2(c - mloc).
+template <int HT, int KT, int NW>
+__device__ __forceinline__ void epi_stats(f32x4 (&acc)[KT][HT], float (&mloc)[HT], int my, int nv, int w, int lane,
+                                          float scale_log2, float *red_m, float *red_s) {
+    const int x = lane & 15, prow = 4 * (lane >> 4);
+    float sloc[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         float mx = -INFINITY;
 #pragma unroll
-        for (int l = 0; l < KT; ++l) mx = fmaxf(mx, fmaxf(fmaxf(acc[l][ht][0], acc[l][ht][1]), fmaxf(acc[l][ht][2], acc[l][ht][3])));
+        for (int l = 0; l < KT; ++l)
+            mx = fmaxf(mx, fmaxf(fmaxf(acc[l][ht][0], acc[l][ht][1]), fmaxf(acc[l][ht][2], acc[l][ht][3])));
         mloc[ht] = cols4_max(mx) * scale_log2;  // -inf for a wave without tiles
     }
 #pragma unroll
@@ -267,7 +268,6 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
     }
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) sloc[ht] = cols4_sum(sloc[ht]);
-    // red_m/red_s laid out [wave][head%16][head tile]: lane x < 16 writes its HT heads at once
     if (lane < 16) {
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
@@ -275,14 +275,22 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
             red_s[(w * 16 + x) * HT + ht] = sloc[ht];
         }
     }
-    __syncthreads();
+}
 
-    // 4. Joint denominator per head, full_h = log2(sum_k 2^c_hk + 2^(nc_lse_h log2 e)):
-    //    lane (g, x) reduces head 16g + x over the waves, then every lane fetches the
-    //    HT heads it holds.  This wave's exp2(c - mloc) values carry weight 2^(mloc - full).
+// After the barrier that publishes red_m/red_s: the joint denominator per head,
+// full_h = log2(sum_k 2^c_hk + 2^(nc_lse_h log2 e)); lane (g, x) reduces head 16g+x over
+// the waves and every lane fetches the HT heads it holds.  This wave's exp2(c - mloc)
+// values carry weight 2^(mloc - full); their head sums m_k (16-lane row reduction) are
+// returned in m and the wave's row mass goes to red_t[w].  nc: the natural-log nc_lse of
+// head 16*min(g, HT-1)+x (ignored when has_nc is false).
+template <int HT, int KT, int NW>
+__device__ __forceinline__ void epi_rows(const f32x4 (&acc)[KT][HT], const float (&mloc)[HT], float (&m)[KT][4], int my,
+                                         int w, int lane, int H, bool has_nc, float nc, const float *red_m,
+                                         const float *red_s, float *red_t) {
+    const int x = lane & 15, g = lane >> 4;
+    const int gg = g < HT ? g : HT - 1;
     float fullv;
     {
-        const int gg = g < HT ? g : HT - 1;
         float M = -INFINITY;
 #pragma unroll 4
         for (int i = 0; i < NW; ++i) M = fmaxf(M, red_m[(i * 16 + x) * HT + gg]);
@@ -291,8 +299,7 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
         for (int i = 0; i < NW; ++i)
             ssum = fmaf(red_s[(i * 16 + x) * HT + gg], fast_exp2(red_m[(i * 16 + x) * HT + gg] - M), ssum);
         fullv = M + fast_log2(ssum);
-        const int h = gg * 16 + x;
-        if (nc_lse != nullptr && h < H) fullv = logaddexp2(fullv, nc_lse[bt * H + h] * kLog2e);
+        if (has_nc && gg * 16 + x < H) fullv = logaddexp2(fullv, nc * kLog2e);
     }
     float wgt[HT];
 #pragma unroll
@@ -300,9 +307,6 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
         const float full = __shfl(fullv, ht * 16 + x);
         wgt[ht] = (ht * 16 + x < H && mloc[ht] != -INFINITY) ? fast_exp2(mloc[ht] - full) : 0.f;
     }
-
-    // 5. Head sum m_k (16-lane row reduction) and the row total.
-    float m[KT][4];
     float part = 0.f;
 #pragma unroll
     for (int l = 0; l < KT; ++l)
@@ -319,13 +323,18 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
         }
     part = cols4_sum(part);
     if (lane == 0) red_t[w] = part;
-    __syncthreads();
+}
+
+// After the barrier that publishes red_t: L1 normalisation and the scatter back to slot
+// order (lane (g, x < 4) stores row 4g + x of each tile).
+template <int KT, int NW>
+__device__ __forceinline__ void epi_scatter(const float (&m)[KT][4], int my, int nv, int w, int lane,
+                                            const float *red_t, float l1_floor, const int32_t *cslot, float *Tr) {
+    const int x = lane & 15, prow = 4 * (lane >> 4);
     float tot = 0.f;
 #pragma unroll 4
     for (int i = 0; i < NW; ++i) tot += red_t[i];
     const float rden = 1.f / fmaxf(tot, l1_floor);
-
-    // 6. Scatter the row back to slot order: lane (g, x < 4) stores row 4g + x of each tile.
     if (x < 4) {
 #pragma unroll
         for (int l = 0; l < KT; ++l) {
@@ -336,6 +345,89 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
             }
         }
     }
+}
+
+// One workgroup per token (latest tokens first, they hold the most valid slots).
+template <int DT, int HT, int KT, int NW>
+__global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kernel(
+    const void *__restrict__ q, const void *__restrict__ pool, const int32_t *__restrict__ idx,
+    const float *__restrict__ nc_lse, int S, int H, int D, int N, int K, float scale_log2, float l1_floor,
+    float *__restrict__ target) {
+    constexpr int EB = Elem<DT>::bytes;
+    constexpr int KP = 2;  // slot passes of NW*64 (K <= 2*NW*64)
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int nch = D >> 5;
+    const int RS = qrow_stride(D, EB);
+    unsigned char *qb = smem;                                                  // [16*HT rows][RS bytes]
+    int32_t *crow = reinterpret_cast<int32_t *>(smem + 16 * HT * RS);         // [K] pool row per compacted slot
+    int32_t *cslot = crow + K;                                                // [K] slot index per compacted slot
+    float *red_m = reinterpret_cast<float *>(cslot + K);                      // [NW][16*HT] per-wave head max
+    float *red_s = red_m + NW * 16 * HT;                                      // [NW][16*HT] per-wave head sum
+    float *red_t = red_s + NW * 16 * HT;                                      // [NW] per-wave row mass
+    int *wcnt = reinterpret_cast<int *>(red_t + NW);                          // [KP][NW] valid-slot counts
+
+    const int64_t bt = (int64_t)gridDim.x - 1 - blockIdx.x;
+    const int b = (int)(bt / S);
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int lane = tid & 63;
+    float *Tr = target + bt * K;
+
+    // 0./1. Query staging (asynchronous) overlaps the slot compaction.
+    stage_queries<DT, HT, NW>(q, bt, H, D, qb, w, lane);
+    const int nv = compact_slots<NW, KP>(idx + bt * K, K, N, Tr, crow, cslot, wcnt, tid, w, lane);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's query loads have landed in LDS
+    __syncthreads();                // ... and everyone else's; the compacted list is complete
+    if (nv == 0) return;            // empty row: already all zeros
+
+    // 2. Scores of this wave's slot tiles: tiles w, w+NW, w+2NW, ... of the compacted list.
+    const int ntiles = (nv + 15) >> 4;
+    const int my = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;
+    const rsrc_t pr = make_rsrc(reinterpret_cast<const char *>(pool) + (size_t)b * N * D * EB,
+                                (uint32_t)((size_t)N * D * EB));
+    // Tiles this wave does not compute stay at -inf: they drop out of the maximum and
+    // their exponentials are exactly 0, so the epilogue needs no per-element masks.
+    f32x4 acc[KT][HT];
+#pragma unroll
+    for (int l = 0; l < KT; ++l) {
+        const float init = l < my ? 0.f : -INFINITY;
+#pragma unroll
+        for (int h = 0; h < HT; ++h) acc[l][h] = f32x4{init, init, init, init};
+    }
+    {
+        uint32_t off[KT];
+#pragma unroll
+        for (int l = 0; l < KT; ++l) {
+            const int pos = 16 * (w + l * NW) + (lane & 15);
+            const int r = (l < my && pos < nv) ? crow[pos] : crow[0];
+            off[l] = (uint32_t)((r * D + 8 * (lane >> 4)) * EB);
+        }
+        if (my > 0) {
+            if constexpr (DT == 0 && KT * HT >= 16)
+                score_dispatch_q1<HT, KT>(my, acc, qb, RS, pr, off, nch, lane);
+            else
+                score_dispatch<DT, HT, KT>(my, acc, qb, RS, pr, off, nch, lane);
+        }
+    }
+
+    // 3.-6. Epilogue: per-head statistics, joint denominators, head sums, normalised scatter.
+    // (lane re-derived from an opaque copy: the epilogue's per-lane addresses are then
+    // computed here instead of being hoisted above the score loop, where they would
+    // compete with its registers)
+    {
+        int t = threadIdx.x;
+        asm volatile("" : "+v"(t));
+        lane = t & 63;
+    }
+    float mloc[HT], m[KT][4];
+    epi_stats<HT, KT, NW>(acc, mloc, my, nv, w, lane, scale_log2, red_m, red_s);
+    __syncthreads();
+    {
+        const int h = 16 * ((lane >> 4) < HT ? (lane >> 4) : HT - 1) + (lane & 15);
+        const float nc = (nc_lse != nullptr && h < H) ? nc_lse[bt * H + h] : 0.f;
+        epi_rows<HT, KT, NW>(acc, mloc, m, my, w, lane, H, nc_lse != nullptr, nc, red_m, red_s, red_t);
+    }
+    __syncthreads();
+    epi_scatter<KT, NW>(m, my, nv, w, lane, red_t, l1_floor, cslot, Tr);
 }
 
 template <int DT, int HT, int KT, int NW>

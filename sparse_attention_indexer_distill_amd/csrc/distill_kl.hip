@@ -7,23 +7,65 @@
 // the KL tail with an analytic backward; MaxText PR "Add Indexer Loss [Deepseek v4]",
 // review comments: log-softmax KL without epsilon, exact gradient Q - P).
 //
-// The row is read once from HBM into registers (each lane holds slots lane + 64e), all
-// reductions are xor-butterflies inside the wave, and the per-row KL plus a per-block
-// (sum, count) partial are written.  A one-block finalize kernel adds the partials in a
-// fixed order, so the loss statistics are bitwise reproducible.
+// The row is read once from HBM into registers (T, z and idx in one round trip, 16-byte
+// loads when K % 4 == 0), all reductions are xor-butterflies inside the wave, and the
+// per-row KL plus a per-block (sum, count) partial are written.  A one-block finalize
+// kernel adds the partials in a fixed order, so the loss statistics are bitwise
+// reproducible.  (A last-block-reduces variant in the same launch needs device-scope
+// fences per block, which write back and invalidate L2 and cost far more than the
+// second launch.)
 #include "sd_device.hpp"
 #include "sd_internal.hpp"
 
 namespace sd {
 namespace {
 
-constexpr int kKlRowsPerBlock = 4;
+constexpr int kKlRowsPerBlock = 8;
 
-template <int EPL>
+// Loads of one row: V = 4 consecutive slots per lane and chunk (16-byte loads, K % 4 == 0)
+// or V = 1 (any K).  Lane l holds slots V*l + 64*V*c + j.  T, z and idx are loaded
+// unconditionally in one round trip (all three are K-long rows); validity is applied
+// afterwards.
+template <int V>
+struct RowIO;
+template <>
+struct RowIO<1> {
+    static __device__ __forceinline__ void load(const float *p, int k, int K, float *o) { o[0] = k < K ? p[k] : 0.f; }
+    static __device__ __forceinline__ void load(const int32_t *p, int k, int K, int *o) { o[0] = k < K ? p[k] : -1; }
+    static __device__ __forceinline__ void store(float *p, int k, int K, const float *v) {
+        if (k < K) p[k] = v[0];
+    }
+};
+template <>
+struct RowIO<4> {
+    static __device__ __forceinline__ void load(const float *p, int k, int K, float *o) {
+        if (k < K) {
+            const f32x4 x = *reinterpret_cast<const f32x4 *>(p + k);
+            o[0] = x[0]; o[1] = x[1]; o[2] = x[2]; o[3] = x[3];
+        } else {
+            o[0] = o[1] = o[2] = o[3] = 0.f;
+        }
+    }
+    static __device__ __forceinline__ void load(const int32_t *p, int k, int K, int *o) {
+        if (k < K) {
+            const u32x4 x = *reinterpret_cast<const u32x4 *>(p + k);
+            o[0] = (int)x[0]; o[1] = (int)x[1]; o[2] = (int)x[2]; o[3] = (int)x[3];
+        } else {
+            o[0] = o[1] = o[2] = o[3] = -1;
+        }
+    }
+    static __device__ __forceinline__ void store(float *p, int k, int K, const float *v) {
+        if (k < K) *reinterpret_cast<f32x4 *>(p + k) = f32x4{v[0], v[1], v[2], v[3]};
+    }
+};
+
+// CH chunks of 64*V slots per row (K <= 64*V*CH).
+template <int V, int CH>
 __global__ __launch_bounds__(kKlRowsPerBlock * 64) void distill_kl_kernel(
     const float *__restrict__ target, const float *__restrict__ logits, const int32_t *__restrict__ idx,
     int64_t rows, int K, int N, float grad_scale, float *__restrict__ kl_rows, float *__restrict__ dlogits,
     float *__restrict__ partials) {
+    constexpr int E = V * CH;
     __shared__ float red_s[kKlRowsPerBlock], red_c[kKlRowsPerBlock];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kKlRowsPerBlock + w;
@@ -32,53 +74,61 @@ __global__ __launch_bounds__(kKlRowsPerBlock * 64) void distill_kl_kernel(
         const float *Tr = target + row * K;
         const float *zr = logits + row * K;
         const int32_t *ir = idx + row * K;
-        float tv[EPL], zv[EPL];
-        bool vv[EPL];
-        float zmax = -INFINITY, sumT = 0.f;
+        float tv[E], zv[E];
+        int iv[E];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int k = V * lane + 64 * V * c;
+            RowIO<V>::load(ir, k, K, iv + V * c);
+            RowIO<V>::load(Tr, k, K, tv + V * c);
+            RowIO<V>::load(zr, k, K, zv + V * c);
+        }
+        // log2 domain: y = z * log2(e)
+        float ymax = -INFINITY, sumT = 0.f;
+        bool vv[E];
         bool any = false;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const int k = lane + 64 * e;
-            const int id = k < K ? ir[k] : -1;
-            vv[e] = k < K && id >= 0 && id < N;
-            tv[e] = vv[e] ? Tr[k] : 0.f;
-            zv[e] = vv[e] ? zr[k] : -INFINITY;
-            zmax = fmaxf(zmax, zv[e]);
+        for (int e = 0; e < E; ++e) {
+            vv[e] = iv[e] >= 0 && iv[e] < N;  // slots past K carry -1
+            tv[e] = vv[e] ? tv[e] : 0.f;
+            zv[e] = vv[e] ? zv[e] * kLog2e : -INFINITY;
+            ymax = fmaxf(ymax, zv[e]);
             sumT += tv[e];
             any = any || vv[e];
         }
+        float *dr = dlogits ? dlogits + row * K : nullptr;
         if (__ballot(any) != 0) {
-            zmax = wave_max(zmax);
+            ymax = wave_max(ymax);
             sumT = wave_sum(sumT);
+            float qv[E];  // softmax numerators 2^(y - ymax) (0 at invalid slots)
             float se = 0.f;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) se += vv[e] ? expf(zv[e] - zmax) : 0.f;
+            for (int e = 0; e < E; ++e) {
+                qv[e] = fast_exp2(zv[e] - ymax);
+                se += qv[e];
+            }
             se = wave_sum(se);
-            const float lse = zmax + logf(se);
-            float kl = 0.f;
+            const float lse2 = ymax + fast_log2(se);  // log2-domain LSE of the valid logits
+            const float rse = 1.f / se;
+            float kl2 = 0.f;  // KL in log2 units: T (log2 T - log2 Q) with log2 Q = y - lse2
 #pragma unroll
-            for (int e = 0; e < EPL; ++e)
-                kl += (vv[e] && tv[e] > 0.f) ? tv[e] * (logf(tv[e]) - (zv[e] - lse)) : 0.f;
-            kl = wave_sum(kl);
-            if (dlogits) {
-                float *dr = dlogits + row * K;
+            for (int e = 0; e < E; ++e) {
+                kl2 += (vv[e] && tv[e] > 0.f) ? tv[e] * (fast_log2(tv[e]) - (zv[e] - lse2)) : 0.f;
+                zv[e] = grad_scale * (sumT * (qv[e] * rse) - tv[e]);  // gradient (0 at invalid slots)
+            }
+            const float kl = wave_sum(kl2) * kLn2;
+            if (dr) {
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    const int k = lane + 64 * e;
-                    if (k < K) dr[k] = vv[e] ? grad_scale * (sumT * expf(zv[e] - lse) - tv[e]) : 0.f;
-                }
+                for (int c = 0; c < CH; ++c) RowIO<V>::store(dr, V * lane + 64 * V * c, K, zv + V * c);
             }
             if (lane == 0) kl_rows[row] = kl;
             rs = kl;
             rc = 1.f;
         } else {
-            if (dlogits) {
-                float *dr = dlogits + row * K;
+            if (dr) {
+                float zero[V] = {};
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    const int k = lane + 64 * e;
-                    if (k < K) dr[k] = 0.f;
-                }
+                for (int c = 0; c < CH; ++c) RowIO<V>::store(dr, V * lane + 64 * V * c, K, zero);
             }
             if (lane == 0) kl_rows[row] = 0.f;
         }
@@ -100,13 +150,21 @@ __global__ __launch_bounds__(kKlRowsPerBlock * 64) void distill_kl_kernel(
     }
 }
 
+// Adds the per-block partials in a fixed order (one block).
 __global__ __launch_bounds__(256) void distill_kl_finalize(const float *__restrict__ partials, int nblk,
                                                            float *__restrict__ stats) {
     __shared__ float ss[256], sc[256];
     float s = 0.f, c = 0.f;
-    for (int i = threadIdx.x; i < nblk; i += 256) {
-        s += partials[2 * (size_t)i];
-        c += partials[2 * (size_t)i + 1];
+    // partials are 8-byte aligned (sum, count) pairs: read two per 16-byte load
+    const int npair2 = nblk >> 1;
+    for (int i = threadIdx.x; i < npair2; i += 256) {
+        const f32x4 v = reinterpret_cast<const f32x4 *>(partials)[i];
+        s += v[0] + v[2];
+        c += v[1] + v[3];
+    }
+    if ((nblk & 1) && threadIdx.x == 0) {
+        s += partials[2 * (size_t)(nblk - 1)];
+        c += partials[2 * (size_t)(nblk - 1) + 1];
     }
     ss[threadIdx.x] = s;
     sc[threadIdx.x] = c;
@@ -124,11 +182,11 @@ __global__ __launch_bounds__(256) void distill_kl_finalize(const float *__restri
     }
 }
 
-template <int EPL>
+template <int V, int CH>
 hipError_t launch_e(const float *target, const float *logits, const int32_t *idx, int64_t rows, int K, int N,
                     float grad_scale, float *kl_rows, float *dlogits, float *stats, float *partials, int nblk,
                     hipStream_t stream) {
-    hipLaunchKernelGGL((distill_kl_kernel<EPL>), dim3(nblk), dim3(kKlRowsPerBlock * 64), 0, stream, target, logits,
+    hipLaunchKernelGGL((distill_kl_kernel<V, CH>), dim3(nblk), dim3(kKlRowsPerBlock * 64), 0, stream, target, logits,
                        idx, rows, K, N, grad_scale, kl_rows, dlogits, partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -151,14 +209,21 @@ hipError_t launch_distill_kl(const float *target, const float *logits, const int
     const int64_t rows = (int64_t)B * S;
     const int nblk = (int)((rows + kKlRowsPerBlock - 1) / kKlRowsPerBlock);
     float *partials = reinterpret_cast<float *>(workspace);
-#define SD_K(E) launch_e<E>(target, logits, idx, rows, K, N, grad_scale, kl_rows, dlogits, stats, partials, nblk, stream)
-    if (K <= 64) return SD_K(1);
-    if (K <= 128) return SD_K(2);
-    if (K <= 256) return SD_K(4);
-    if (K <= 512) return SD_K(8);
-    if (K <= 1024) return SD_K(16);
-    if (K <= 2048) return SD_K(32);
-    return SD_K(64);
+#define SD_K(V, C) launch_e<V, C>(target, logits, idx, rows, K, N, grad_scale, kl_rows, dlogits, stats, partials, nblk, stream)
+    if (K % 4 == 0) {  // 16-byte rows and loads
+        if (K <= 256) return SD_K(4, 1);
+        if (K <= 512) return SD_K(4, 2);
+        if (K <= 1024) return SD_K(4, 4);
+        if (K <= 2048) return SD_K(4, 8);
+        return SD_K(4, 16);
+    }
+    if (K <= 64) return SD_K(1, 1);
+    if (K <= 128) return SD_K(1, 2);
+    if (K <= 256) return SD_K(1, 4);
+    if (K <= 512) return SD_K(1, 8);
+    if (K <= 1024) return SD_K(1, 16);
+    if (K <= 2048) return SD_K(1, 32);
+    return SD_K(1, 64);
 #undef SD_K
 }
 

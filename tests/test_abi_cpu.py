@@ -100,7 +100,9 @@ def _kl(lib, T=FAKE, z=FAKE, idx=FAKE, B=1, S=8, K=4, N=2, g=1.0, rows=FAKE, dz=
 
 
 def test_distill_kl_rejections(lib):
-    assert lib.distill_kl_workspace_bytes(1, 8, 4) == 2 * 2 * 4
+    # 2 floats (sum, count) per 8-row block
+    assert lib.distill_kl_workspace_bytes(1, 8, 4) == 1 * 2 * 4
+    assert lib.distill_kl_workspace_bytes(1, 12, 4) == 2 * 2 * 4
     assert lib.distill_kl_workspace_bytes(0, 8, 4) == 0
     assert _kl(lib, T=None) == sd.SD_ERR_NULL_ARG
     assert _kl(lib, rows=None) == sd.SD_ERR_NULL_ARG
@@ -108,7 +110,7 @@ def test_distill_kl_rejections(lib):
     assert _kl(lib, ws=None) == sd.SD_ERR_NULL_ARG
     assert _kl(lib, N=0) == sd.SD_ERR_BAD_SHAPE
     assert _kl(lib, g=float("nan")) == sd.SD_ERR_BAD_SHAPE
-    assert _kl(lib, wsb=15) == sd.SD_ERR_BAD_SHAPE
+    assert _kl(lib, wsb=7) == sd.SD_ERR_BAD_SHAPE  # one 8-row block needs 8 bytes
     assert b"workspace" in lib.sd_last_error()
     assert _kl(lib, K=4097) == sd.SD_ERR_UNSUPPORTED
 

@@ -237,6 +237,35 @@ def test_kl_isolated_all_configs():
         assert torch.equal(kl2, kl) and torch.equal(st2, st)
 
 
+def test_kl_shared_workspace_across_calls():
+    """One workspace serves consecutive calls of different sizes (stale partials from a
+    larger call never leak into a smaller one), and stats match the oracle each time."""
+    sd = _sd()
+    dev = _dev()
+    cases = [("c2", None), ("c1", None), ("c2", 7)]
+    big = max(sd.distill_kl_workspace_bytes(synth.CONFIGS[n].B, synth.CONFIGS[n].S, synth.CONFIGS[n].K)
+              for n, _ in cases)
+    ws = torch.full((big,), 0x7F, dtype=torch.uint8, device=dev)  # garbage, not zeros
+    for name, seed in cases:
+        c = synth.CONFIGS[name]
+        x = synth.make_inputs(name)
+        idx = x["idx"]
+        rng = np.random.default_rng(c.cid if seed is None else seed)
+        valid = ((idx >= 0) & (idx < c.N)).numpy()
+        r = rng.random(idx.shape).astype(np.float32) * valid
+        sm = r.sum(-1, keepdims=True)
+        T = np.where(sm > 0, r / np.where(sm > 0, sm, 1), 0).astype(np.float32)
+        z = rng.standard_normal(idx.shape).astype(np.float32)
+        _say(f"[gpu] {name}: KL with a shared workspace (seed {seed})")
+        kl, dz, st = sd.distill_kl_fwd_bwd(torch.from_numpy(T).to(dev), torch.from_numpy(z).to(dev),
+                                           idx.to(dev), c.N, grad_scale=1.0, workspace=ws)
+        torch.cuda.synchronize()
+        _, _, st_ref = oracle.kl(T, z, idx, c.N, grad_scale=1.0)
+        stn = _np(st)
+        assert stn[1] == st_ref[1]
+        assert abs(stn[0] - st_ref[0]) <= KL_RTOL * abs(st_ref[0])
+
+
 # ------------------------------------------------------------------ edge shapes
 EDGE = [
     # (name, B, S, H, D, N, K, W, dtype, segments)

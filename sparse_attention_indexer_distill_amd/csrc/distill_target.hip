@@ -51,19 +51,27 @@ __device__ __forceinline__ typename Elem<DT>::frag_t q_frag(const unsigned char 
 // gathered pool fragments (buffer loads) and the query fragments (LDS) of chunk c+1 are
 // in flight while chunk c's MFMAs run.  MY is a compile-time count, so the loop has no
 // per-tile branches.
+//
+// cr rotates the chunk order (chunk c is D-chunk (c + cr) mod nch): waves of a token and
+// tokens in flight start at different offsets of their rows, which spreads the gathers
+// over the L2 channels (7% at D = 512).  The sum order stays fixed per (token, wave).
 template <int DT, int HT, int MY, int KT>
 __device__ __forceinline__ void score_tiles(f32x4 (&acc)[KT][HT], const unsigned char *__restrict__ qb, int RS, rsrc_t pool,
-                                            const uint32_t (&off)[KT], int nch, int lane) {
+                                            const uint32_t (&off)[KT], int nch, int cr, int lane) {
     using frag_t = typename Elem<DT>::frag_t;
     constexpr uint32_t CB = 32 * Elem<DT>::bytes;  // bytes of one 32-element chunk of a row
     frag_t a0[MY], a1[MY], b0[HT], b1[HT];
+    auto rot = [&](int c) {
+        const int cc = c + cr;
+        return cc >= nch ? cc - nch : cc;
+    };
     auto load_a = [&](frag_t(&a)[MY], int c) {
 #pragma unroll
-        for (int l = 0; l < MY; ++l) a[l] = buf_load_frag<DT>(pool, off[l] + (uint32_t)c * CB);
+        for (int l = 0; l < MY; ++l) a[l] = buf_load_frag<DT>(pool, off[l] + (uint32_t)rot(c) * CB);
     };
     auto load_b = [&](frag_t(&bq)[HT], int c) {
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) bq[ht] = q_frag<DT, HT>(qb, RS, ht, c, lane);
+        for (int ht = 0; ht < HT; ++ht) bq[ht] = q_frag<DT, HT>(qb, RS, ht, rot(c), lane);
     };
     auto mma = [&](const frag_t(&a)[MY], const frag_t(&bq)[HT]) {
 #pragma unroll
@@ -100,17 +108,21 @@ __device__ __forceinline__ void score_tiles(f32x4 (&acc)[KT][HT], const unsigned
 // which frees 4*HT registers per lane -- enough to keep the widest tile set spill-free.
 template <int HT, int MY, int KT>
 __device__ __forceinline__ void score_tiles_q1(f32x4 (&acc)[KT][HT], const unsigned char *__restrict__ qb, int RS,
-                                               rsrc_t pool, const uint32_t (&off)[KT], int nch, int lane) {
+                                               rsrc_t pool, const uint32_t (&off)[KT], int nch, int cr, int lane) {
     constexpr uint32_t CB = 64;  // bytes of one 32-element bf16 chunk of a row
     u32x4 a0[MY], a1[MY];
+    auto rot = [&](int c) {
+        const int cc = c + cr;
+        return cc >= nch ? cc - nch : cc;
+    };
     auto load_a = [&](u32x4(&a)[MY], int c) {
 #pragma unroll
-        for (int l = 0; l < MY; ++l) a[l] = buf_load16(pool, off[l] + (uint32_t)c * CB);
+        for (int l = 0; l < MY; ++l) a[l] = buf_load16(pool, off[l] + (uint32_t)rot(c) * CB);
     };
     auto mma = [&](const u32x4(&a)[MY], int c) {
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
-            const u32x4 b = q_frag<0, HT>(qb, RS, ht, c, lane);
+            const u32x4 b = q_frag<0, HT>(qb, RS, ht, rot(c), lane);
 #pragma unroll
             for (int l = 0; l < MY; ++l) acc[l][ht] = mfma_frag<0>(a[l], b, acc[l][ht]);
         }
@@ -136,21 +148,22 @@ __device__ __forceinline__ void score_tiles_q1(f32x4 (&acc)[KT][HT], const unsig
 
 template <int HT, int KT, int MY = KT>
 __device__ __forceinline__ void score_dispatch_q1(int my, f32x4 (&acc)[KT][HT], const unsigned char *__restrict__ qb,
-                                                  int RS, rsrc_t pool, const uint32_t (&off)[KT], int nch, int lane) {
+                                                  int RS, rsrc_t pool, const uint32_t (&off)[KT], int nch, int cr,
+                                                  int lane) {
     if (my == MY) {
-        score_tiles_q1<HT, MY, KT>(acc, qb, RS, pool, off, nch, lane);
+        score_tiles_q1<HT, MY, KT>(acc, qb, RS, pool, off, nch, cr, lane);
     } else if constexpr (MY > 1) {
-        score_dispatch_q1<HT, KT, MY - 1>(my, acc, qb, RS, pool, off, nch, lane);
+        score_dispatch_q1<HT, KT, MY - 1>(my, acc, qb, RS, pool, off, nch, cr, lane);
     }
 }
 
 template <int DT, int HT, int KT, int MY = KT>
 __device__ __forceinline__ void score_dispatch(int my, f32x4 (&acc)[KT][HT], const unsigned char *__restrict__ qb, int RS,
-                                               rsrc_t pool, const uint32_t (&off)[KT], int nch, int lane) {
+                                               rsrc_t pool, const uint32_t (&off)[KT], int nch, int cr, int lane) {
     if (my == MY) {
-        score_tiles<DT, HT, MY, KT>(acc, qb, RS, pool, off, nch, lane);
+        score_tiles<DT, HT, MY, KT>(acc, qb, RS, pool, off, nch, cr, lane);
     } else if constexpr (MY > 1) {
-        score_dispatch<DT, HT, KT, MY - 1>(my, acc, qb, RS, pool, off, nch, lane);
+        score_dispatch<DT, HT, KT, MY - 1>(my, acc, qb, RS, pool, off, nch, cr, lane);
     }
 }
 
@@ -401,11 +414,13 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
             const int r = (l < my && pos < nv) ? crow[pos] : crow[0];
             off[l] = (uint32_t)((r * D + 8 * (lane >> 4)) * EB);
         }
+        // chunk rotation: even (keeps the chunk pairs of the pipelined loop), per wave and token
+        const int cr = (nch & 1) ? 0 : (2 * (5 * w + (int)(bt % nch))) % nch;
         if (my > 0) {
             if constexpr (DT == 0 && KT * HT >= 16)
-                score_dispatch_q1<HT, KT>(my, acc, qb, RS, pr, off, nch, lane);
+                score_dispatch_q1<HT, KT>(my, acc, qb, RS, pr, off, nch, cr, lane);
             else
-                score_dispatch<DT, HT, KT>(my, acc, qb, RS, pr, off, nch, lane);
+                score_dispatch<DT, HT, KT>(my, acc, qb, RS, pr, off, nch, cr, lane);
         }
     }
 

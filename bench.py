@@ -35,6 +35,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "ms per CSA layer (target+window_lse+KL fwd/bwd), % MFMA/HBM roofline"
 KERNEL_SOURCES = {
     "distill_target": "sparse_attention_indexer_distill_amd/csrc/distill_target.hip",
+    "distill_target_fused": "sparse_attention_indexer_distill_amd/csrc/distill_target.hip",
     "window_lse": "sparse_attention_indexer_distill_amd/csrc/window_lse.hip",
     "distill_kl_fwd_bwd": "sparse_attention_indexer_distill_amd/csrc/distill_kl.hip",
 }
@@ -77,6 +78,11 @@ def algorithmic_work(cfg, x) -> dict:
                                bytes=B * S * H * D * e + B * N * D * e + B * S * K * 4 + B * S * H * 4 + B * S * K * 4,
                                pairs=valid),
         "distill_kl_fwd_bwd": dict(flops=10 * valid, bytes=B * S * K * 4 * 4 + B * S * 4 + 8, pairs=valid),
+        # window part and compressed part in one pass: q read once; kwin, pool, idx read; T and nc written
+        "distill_target_fused": dict(flops=2 * H * D * (wp + valid),
+                                     bytes=B * S * H * D * e + B * S * D * e + B * N * D * e + B * S * K * 4 +
+                                     B * S * K * 4 + B * S * H * 4 + H * 4 + seg_b,
+                                     pairs=wp + valid),
     }
 
 
@@ -125,6 +131,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c3", choices=["c3", "c4", "c5"])
+    ap.add_argument("--path", default="3call", choices=["3call", "fused"],
+                    help="3call: window_lse -> distill_target -> KL; fused: distill_target_fused -> KL")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB three times (reference for HBM byte counters)")
@@ -156,22 +164,31 @@ def main() -> int:
     nonempty = int(((x["idx"] >= 0) & (x["idx"] < cfg.N)).any(-1).sum())
     grad_scale = 1e-2 / nonempty          # loss coefficient 1e-2, mean over non-empty rows
 
-    names = ["window_lse", "distill_target", "distill_kl_fwd_bwd"]
+    fused = args.path == "fused"
+    names = ["distill_target_fused", "distill_kl_fwd_bwd"] if fused else ["window_lse", "distill_target",
+                                                                           "distill_kl_fwd_bwd"]
 
     def step(ev=None):
+        j = 0
         if ev is not None:
-            ev[0].record()
-        sd.window_lse(g["q"], g["kwin"], g["sink"], g["seg"], W=cfg.W, out=bufs["nc_lse"])
+            ev[j].record()
+        if fused:
+            sd.distill_target_fused(g["q"], g["kwin"], g["pool"], g["idx"], g["sink"], g["seg"], W=cfg.W,
+                                    out=bufs["target"], nc_out=bufs["nc_lse"])
+        else:
+            sd.window_lse(g["q"], g["kwin"], g["sink"], g["seg"], W=cfg.W, out=bufs["nc_lse"])
+            if ev is not None:
+                j += 1
+                ev[j].record()
+            sd.distill_target(g["q"], g["pool"], g["idx"], bufs["nc_lse"], out=bufs["target"])
         if ev is not None:
-            ev[1].record()
-        sd.distill_target(g["q"], g["pool"], g["idx"], bufs["nc_lse"], out=bufs["target"])
-        if ev is not None:
-            ev[2].record()
+            j += 1
+            ev[j].record()
         sd.distill_kl_fwd_bwd(bufs["target"], g["z"], g["idx"], cfg.N, grad_scale=grad_scale,
                               kl_rows=bufs["kl_rows"], dlogits=bufs["dlogits"], stats=bufs["stats"],
                               workspace=bufs["workspace"])
         if ev is not None:
-            ev[3].record()
+            ev[j + 1].record()
 
     for _ in range(args.warmup):
         step()
@@ -183,7 +200,7 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     # timed region 2: the same steps with HIP events between the kernels (per-kernel time)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(evs[i])
@@ -202,7 +219,7 @@ def main() -> int:
                       "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
                       "algorithmic_flops": work[n]["flops"], "algorithmic_bytes": work[n]["bytes"],
                       "src": src_hash(n)}
-    dom = "distill_target"
+    dom = "distill_target_fused" if fused else "distill_target"
     ach = kernels[dom]["TFLOP/s"]
     roofline = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": read_traffic(dom, args.workload)}
@@ -216,7 +233,8 @@ def main() -> int:
                    "global_batch": B, "seq_len": S, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "kernels": kernels,
-        "layer_useful_TFLOP/s": round(sum(w["flops"] for w in work.values()) / (ms_per_step * 1e-3) / 1e12, 1),
+        "path": args.path,
+        "layer_useful_TFLOP/s": round(sum(work[n]["flops"] for n in names) / (ms_per_step * 1e-3) / 1e12, 1),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, x, kern_total)

@@ -106,6 +106,27 @@ int distill_target(const void *q, const void *pool, const int32_t *idx, const fl
                    int dtype, float *target, hipStream_t stream);
 
 /*
+ * distill_target_fused -- distill_target with its window part computed in the same pass.
+ *
+ *   nc_h   = log( sum_{j in win(t)} exp(scale * <q[b,t,h,:], kwin[b,j,:]>) + exp(sink[h]) )
+ *   then exactly as distill_target with nc_lse = nc.
+ *
+ * The joint softmax runs over the window keys, the selected compressed rows and the sink
+ * at once (the target defined by the Primus PR "perf(deepseek-v4): fuse and enable the
+ * indexer distillation loss", body "Why the target was wrong", computed from the
+ * attention's own entries), so the queries are read from HBM once for the whole target
+ * instead of once by window_lse and once by distill_target.  win(t), sink and seg as in
+ * window_lse; pool, idx, l1_floor and target as in distill_target.
+ *
+ *   nc_lse_out [B,S,H] float32 out or NULL: the window+sink LSE (what window_lse returns)
+ * Limits: those of window_lse and distill_target together; scale positive and finite.
+ */
+int distill_target_fused(const void *q, const void *kwin, const float *sink, const int32_t *seg,
+                         const void *pool, const int32_t *idx, int B, int S, int H, int D, int N,
+                         int K, int W, float scale, float l1_floor, int dtype, float *target,
+                         float *nc_lse_out, hipStream_t stream);
+
+/*
  * distill_kl_fwd_bwd -- KL(target || softmax(logits)) per row, fused with its gradient.
  *
  *   V       = valid slots of the row;  lse = log sum_{k in V} exp(logits_k)

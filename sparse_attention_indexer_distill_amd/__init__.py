@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["window_lse", "distill_target", "distill_kl_fwd_bwd", "distill_kl_workspace_bytes",
+__all__ = ["window_lse", "distill_target", "distill_target_fused", "distill_kl_fwd_bwd", "distill_kl_workspace_bytes",
            "csa_distill_layer", "library_path", "load_library", "SD_BF16", "SD_F32"]
 
 SD_OK, SD_ERR_NULL_ARG, SD_ERR_BAD_SHAPE, SD_ERR_UNSUPPORTED, SD_ERR_DTYPE, SD_ERR_HIP = range(6)
@@ -54,6 +54,9 @@ def load_library():
     lib.window_lse.restype = _i
     lib.distill_target.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _f, _i, _vp, _vp]
     lib.distill_target.restype = _i
+    lib.distill_target_fused.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _f, _i, _vp,
+                                         _vp, _vp]
+    lib.distill_target_fused.restype = _i
     lib.distill_kl_workspace_bytes.argtypes = [_i, _i, _i]
     lib.distill_kl_workspace_bytes.restype = ctypes.c_size_t
     lib.distill_kl_fwd_bwd.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
@@ -165,6 +168,53 @@ def distill_target(q: torch.Tensor, pool: torch.Tensor, idx: torch.Tensor,
     return out
 
 
+def distill_target_fused(q: torch.Tensor, kwin: torch.Tensor, pool: torch.Tensor, idx: torch.Tensor,
+                         sink: Optional[torch.Tensor] = None, seg: Optional[torch.Tensor] = None, *, W: int,
+                         scale: Optional[float] = None, l1_floor: float = 0.0, want_nc: bool = False,
+                         out: Optional[torch.Tensor] = None, nc_out: Optional[torch.Tensor] = None,
+                         stream=None):
+    """KL target [B,S,K] fp32 with the window part computed in the same pass (one read of q).
+    Returns target, or (target, nc_lse) when want_nc or nc_out is given."""
+    lib = load_library()
+    dev = q.device
+    q = _dev(q, "q", dev)
+    kwin = _dev(kwin, "kwin", dev)
+    pool = _dev(pool, "pool", dev)
+    B, S, H, D = q.shape
+    if kwin.shape != (B, S, D) or kwin.dtype != q.dtype:
+        raise ValueError(f"kwin must be [{B},{S},{D}] {q.dtype}, got {tuple(kwin.shape)} {kwin.dtype}")
+    if pool.dim() != 3 or pool.shape[0] != B or pool.shape[2] != D or pool.dtype != q.dtype:
+        raise ValueError(f"pool must be [{B},N,{D}] {q.dtype}, got {tuple(pool.shape)} {pool.dtype}")
+    N = pool.shape[1]
+    if idx.dim() != 3 or idx.shape[:2] != (B, S):
+        raise ValueError(f"idx must be [{B},{S},K]")
+    idx = _dev(idx.to(torch.int32), "idx", dev)
+    K = idx.shape[2]
+    if sink is not None:
+        sink = _dev(sink.detach().to(torch.float32), "sink", dev)
+        if sink.numel() != H:
+            raise ValueError(f"sink must hold {H} head values, got {sink.numel()}")
+    if seg is not None:
+        seg = _dev(seg.to(torch.int32), "seg", dev)
+        if seg.shape != (B, S):
+            raise ValueError(f"seg must be [{B},{S}]")
+    if out is None:
+        out = torch.empty((B, S, K), dtype=torch.float32, device=dev)
+    elif out.shape != (B, S, K) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B,S,K] tensor")
+    if nc_out is None and want_nc:
+        nc_out = torch.empty((B, S, H), dtype=torch.float32, device=dev)
+    if nc_out is not None and (nc_out.shape != (B, S, H) or nc_out.dtype != torch.float32
+                               or not nc_out.is_contiguous()):
+        raise ValueError("nc_out must be a contiguous float32 [B,S,H] tensor")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib.distill_target_fused(_ptr(q), _ptr(kwin), _ptr(sink), _ptr(seg), _ptr(pool), _ptr(idx), B, S, H, D, N,
+                                  K, int(W), scale, float(l1_floor), _dtype_code(q), _ptr(out), _ptr(nc_out),
+                                  _stream(dev, stream))
+    _check(st, "distill_target_fused")
+    return (out, nc_out) if nc_out is not None else out
+
+
 def distill_kl_workspace_bytes(B: int, S: int, K: int) -> int:
     return int(load_library().distill_kl_workspace_bytes(B, S, K))
 
@@ -207,13 +257,18 @@ def distill_kl_fwd_bwd(target: torch.Tensor, logits: torch.Tensor, idx: torch.Te
 
 def csa_distill_layer(q, kwin, pool, idx, logits, sink=None, seg=None, *, W: int,
                       scale: Optional[float] = None, grad_scale: float = 1.0, want_grad: bool = True,
-                      bufs: Optional[dict] = None, stream=None):
-    """One CSA layer's distillation step: window_lse -> distill_target -> distill_kl_fwd_bwd.
+                      fused: bool = False, bufs: Optional[dict] = None, stream=None):
+    """One CSA layer's distillation step: window_lse -> distill_target -> distill_kl_fwd_bwd, or
+    with fused=True distill_target_fused -> distill_kl_fwd_bwd (same outputs, one read of q).
     ``bufs`` may hold preallocated outputs (nc_lse, target, kl_rows, dlogits, stats, workspace).
     Returns a dict with every output."""
     bufs = {} if bufs is None else bufs
-    nc = window_lse(q, kwin, sink, seg, W=W, scale=scale, out=bufs.get("nc_lse"), stream=stream)
-    T = distill_target(q, pool, idx, nc, scale=scale, out=bufs.get("target"), stream=stream)
+    if fused:
+        T, nc = distill_target_fused(q, kwin, pool, idx, sink, seg, W=W, scale=scale, want_nc=True,
+                                     out=bufs.get("target"), nc_out=bufs.get("nc_lse"), stream=stream)
+    else:
+        nc = window_lse(q, kwin, sink, seg, W=W, scale=scale, out=bufs.get("nc_lse"), stream=stream)
+        T = distill_target(q, pool, idx, nc, scale=scale, out=bufs.get("target"), stream=stream)
     kl, dz, st = distill_kl_fwd_bwd(T, logits, idx, pool.shape[1], grad_scale=grad_scale, want_grad=want_grad,
                                     kl_rows=bufs.get("kl_rows"), dlogits=bufs.get("dlogits"),
                                     stats=bufs.get("stats"), workspace=bufs.get("workspace"), stream=stream)

@@ -86,6 +86,24 @@ int distill_target(const void *q, const void *pool, const int32_t *idx, const fl
                       "distill_target launch");
 }
 
+int distill_target_fused(const void *q, const void *kwin, const float *sink, const int32_t *seg, const void *pool,
+                         const int32_t *idx, int B, int S, int H, int D, int N, int K, int W, float scale,
+                         float l1_floor, int dtype, float *target, float *nc_lse_out, hipStream_t stream) {
+    if (!q || !kwin || !pool || !idx || !target)
+        return fail(SD_ERR_NULL_ARG, "distill_target_fused: q, kwin, pool, idx and target are required");
+    int st = check_common(dtype, B, S, H, D);
+    if (st != SD_OK) return st;
+    if (N <= 0 || K <= 0) return fail(SD_ERR_BAD_SHAPE, "distill_target_fused: N=%d and K=%d must be positive", N, K);
+    if (W <= 0) return fail(SD_ERR_BAD_SHAPE, "distill_target_fused: W=%d must be positive", W);
+    if (K > sd::kMaxTopK) return fail(SD_ERR_UNSUPPORTED, "distill_target_fused: K=%d exceeds %d", K, sd::kMaxTopK);
+    if (W > sd::kMaxWindow) return fail(SD_ERR_UNSUPPORTED, "distill_target_fused: W=%d exceeds %d", W, sd::kMaxWindow);
+    if (!isfinite(scale) || !(scale > 0.f) || isnan(l1_floor))
+        return fail(SD_ERR_BAD_SHAPE, "distill_target_fused: scale must be positive and finite, l1_floor not NaN");
+    return hip_status(sd::launch_distill_target_fused(q, kwin, sink, seg, pool, idx, B, S, H, D, N, K, W, scale,
+                                                      l1_floor, dtype, target, nc_lse_out, stream),
+                      "distill_target_fused launch");
+}
+
 size_t distill_kl_workspace_bytes(int B, int S, int K) {
     if (B <= 0 || S <= 0 || K <= 0) return 0;
     return sd::kl_workspace_bytes(B, S, K);

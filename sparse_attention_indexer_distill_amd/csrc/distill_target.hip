@@ -360,42 +360,154 @@ __device__ __forceinline__ void epi_scatter(const float (&m)[KT][4], int my, int
     }
 }
 
-// One workgroup per token (latest tokens first, they hold the most valid slots).
-template <int DT, int HT, int KT, int NW>
-__global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kernel(
-    const void *__restrict__ q, const void *__restrict__ pool, const int32_t *__restrict__ idx,
-    const float *__restrict__ nc_lse, int S, int H, int D, int N, int K, float scale_log2, float l1_floor,
-    float *__restrict__ target) {
+// Arguments of the target kernels (one struct in the kernel-argument segment).
+struct TargetArgs {
+    const void *q, *pool;
+    const int32_t *idx;
+    const float *nc_lse;  // natural-log window+sink LSE per (b,t,h), or NULL (legacy)
+    // fused form only: the window part is computed in the kernel
+    const void *kwin;
+    const float *sink;    // [H] or NULL
+    const int32_t *seg;   // [B,S] or NULL
+    float *nc_out;        // [B,S,H] or NULL: the window+sink LSE as a by-product
+    int W;
+    int B, S, H, D, N, K;
+    float scale_log2, l1_floor;
+    float *target;
+};
+
+// Window part of the joint softmax for token t of batch b, inside the target kernel:
+// the LSE over {scale <q_h, kwin_j> : j in [max(0, t-W+1), t], seg[j] == seg[t]} plus the
+// sink, per head.  Window tiles of 16 consecutive keys starting at the first key are dealt
+// to the waves like slot tiles (at most KWT per wave) and scored with the same MFMA loop
+// against the staged queries; masked per-wave statistics are combined through red_wm/red_ws
+// (one barrier).  Returns, in natural log, the value of head 16*min(g, HT-1) + x for lane
+// (g, x) -- the layout the epilogue takes its nc values in.
+template <int DT, int HT, int NW, int KWT>
+__device__ __forceinline__ float window_part(const TargetArgs &a, const unsigned char *qb, int RS, int b, int t, int w,
+                                             int lane, float *red_wm, float *red_ws) {
     constexpr int EB = Elem<DT>::bytes;
-    constexpr int KP = 2;  // slot passes of NW*64 (K <= 2*NW*64)
+    const int S = a.S, D = a.D, nch = D >> 5;
+    const int kf = t - a.W + 1 > 0 ? t - a.W + 1 : 0;
+    const int nwt = (t - kf + 16) >> 4;
+    const int myw = nwt > w ? (nwt - w + NW - 1) / NW : 0;
+    const rsrc_t kr = make_rsrc(reinterpret_cast<const char *>(a.kwin) + (size_t)b * S * D * EB,
+                                (uint32_t)((size_t)S * D * EB));
+    f32x4 acc[KWT][HT];
+#pragma unroll
+    for (int l = 0; l < KWT; ++l) {
+        const float init = l < myw ? 0.f : -INFINITY;
+#pragma unroll
+        for (int h = 0; h < HT; ++h) acc[l][h] = f32x4{init, init, init, init};
+    }
+    if (myw > 0) {
+        uint32_t off[KWT];
+#pragma unroll
+        for (int l = 0; l < KWT; ++l) {
+            int r = kf + 16 * (w + l * NW) + (lane & 15);
+            r = r < t ? r : t;  // rows past t are loaded as row t and masked below
+            off[l] = (uint32_t)((r * D + 8 * (lane >> 4)) * EB);
+        }
+        score_dispatch<DT, HT, KWT>(myw, acc, qb, RS, kr, off, nch, 0, lane);
+    }
+    // masked statistics (log2 domain); key j of element (l, i) = kf + 16(w + l*NW) + 4g + i
+    const int x = lane & 15, g = lane >> 4;
+    const int sg_t = a.seg ? a.seg[(size_t)b * S + t] : 0;
+    bool okj[KWT][4];
+#pragma unroll
+    for (int l = 0; l < KWT; ++l)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = kf + 16 * (w + l * NW) + 4 * g + i;
+            okj[l][i] = l < myw && j <= t && (a.seg == nullptr || a.seg[(size_t)b * S + j] == sg_t);
+        }
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int l = 0; l < KWT; ++l)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = okj[l][i] ? fmaxf(mx, acc[l][ht][i] * a.scale_log2) : mx;
+        mx = cols4_max(mx);
+        float sum = 0.f;
+#pragma unroll
+        for (int l = 0; l < KWT; ++l)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sum += okj[l][i] ? fast_exp2(fmaf(acc[l][ht][i], a.scale_log2, -mx)) : 0.f;
+        sum = cols4_sum(sum);
+        if (lane < 16) {
+            red_wm[(w * 16 + x) * HT + ht] = mx;
+            red_ws[(w * 16 + x) * HT + ht] = sum;
+        }
+    }
+    __syncthreads();
+    const int gg = g < HT ? g : HT - 1;
+    float M = -INFINITY;
+#pragma unroll 4
+    for (int i = 0; i < NW; ++i) M = fmaxf(M, red_wm[(i * 16 + x) * HT + gg]);
+    float ssum = 0.f;  // key t is always in its own window, so M is finite
+#pragma unroll 4
+    for (int i = 0; i < NW; ++i) {
+        const float mi = red_wm[(i * 16 + x) * HT + gg];
+        ssum += mi == -INFINITY ? 0.f : red_ws[(i * 16 + x) * HT + gg] * fast_exp2(mi - M);
+    }
+    float nc2 = M + fast_log2(ssum);
+    const int h = gg * 16 + x;
+    if (a.sink != nullptr && h < a.H) nc2 = logaddexp2(nc2, a.sink[h] * kLog2e);
+    return nc2 * kLn2;
+}
+
+// One workgroup per token (latest tokens first, they hold the most valid slots).  FUSED:
+// the window part of the joint softmax is computed here too (window_part) instead of being
+// read from nc_lse, so the queries are read from HBM once for the whole target.
+template <int DT, int HT, int KT, int NW, bool FUSED>
+__global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kernel(const TargetArgs a) {
+    constexpr int EB = Elem<DT>::bytes;
+    constexpr int KP = 2;                      // slot passes of NW*64 (K <= 2*NW*64)
+    constexpr int KWT = (8 + NW - 1) / NW;     // window tiles per wave (W <= 128)
     extern __shared__ __align__(16) unsigned char smem[];
+    const int S = a.S, H = a.H, D = a.D, N = a.N, K = a.K;
     const int nch = D >> 5;
     const int RS = qrow_stride(D, EB);
     unsigned char *qb = smem;                                                  // [16*HT rows][RS bytes]
     int32_t *crow = reinterpret_cast<int32_t *>(smem + 16 * HT * RS);         // [K] pool row per compacted slot
     int32_t *cslot = crow + K;                                                // [K] slot index per compacted slot
-    float *red_m = reinterpret_cast<float *>(cslot + K);                      // [NW][16*HT] per-wave head max
-    float *red_s = red_m + NW * 16 * HT;                                      // [NW][16*HT] per-wave head sum
+    float *red_m = reinterpret_cast<float *>(cslot + K);                      // [NW][16][HT] per-wave head max
+    float *red_s = red_m + NW * 16 * HT;                                      // [NW][16][HT] per-wave head sum
     float *red_t = red_s + NW * 16 * HT;                                      // [NW] per-wave row mass
     int *wcnt = reinterpret_cast<int *>(red_t + NW);                          // [KP][NW] valid-slot counts
+    float *red_wm = reinterpret_cast<float *>(wcnt + KP * NW);                // FUSED: [NW][16][HT] window max
+    float *red_ws = red_wm + NW * 16 * HT;                                    // FUSED: [NW][16][HT] window sum
 
     const int64_t bt = (int64_t)gridDim.x - 1 - blockIdx.x;
     const int b = (int)(bt / S);
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     int lane = tid & 63;
-    float *Tr = target + bt * K;
+    float *Tr = a.target + bt * K;
 
     // 0./1. Query staging (asynchronous) overlaps the slot compaction.
-    stage_queries<DT, HT, NW>(q, bt, H, D, qb, w, lane);
-    const int nv = compact_slots<NW, KP>(idx + bt * K, K, N, Tr, crow, cslot, wcnt, tid, w, lane);
+    stage_queries<DT, HT, NW>(a.q, bt, H, D, qb, w, lane);
+    const int nv = compact_slots<NW, KP>(a.idx + bt * K, K, N, Tr, crow, cslot, wcnt, tid, w, lane);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's query loads have landed in LDS
     __syncthreads();                // ... and everyone else's; the compacted list is complete
+
+    // nc value (natural log) of head 16*min(g, HT-1) + x for lane (g, x)
+    float nc = 0.f;
+    if constexpr (FUSED) {
+        nc = window_part<DT, HT, NW, KWT>(a, qb, RS, b, (int)(bt - (int64_t)b * S), w, lane, red_wm, red_ws);
+        const int g = lane >> 4, h = 16 * g + (lane & 15);
+        if (a.nc_out != nullptr && g < HT && h < H) a.nc_out[bt * H + h] = nc;
+    } else {
+        const int h = 16 * ((lane >> 4) < HT ? (lane >> 4) : HT - 1) + (lane & 15);
+        if (a.nc_lse != nullptr && h < H) nc = a.nc_lse[bt * H + h];
+    }
     if (nv == 0) return;            // empty row: already all zeros
 
     // 2. Scores of this wave's slot tiles: tiles w, w+NW, w+2NW, ... of the compacted list.
     const int ntiles = (nv + 15) >> 4;
     const int my = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;
-    const rsrc_t pr = make_rsrc(reinterpret_cast<const char *>(pool) + (size_t)b * N * D * EB,
+    const rsrc_t pr = make_rsrc(reinterpret_cast<const char *>(a.pool) + (size_t)b * N * D * EB,
                                 (uint32_t)((size_t)N * D * EB));
     // Tiles this wave does not compute stay at -inf: they drop out of the maximum and
     // their exponentials are exactly 0, so the epilogue needs no per-element masks.
@@ -434,55 +546,57 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
         lane = t & 63;
     }
     float mloc[HT], m[KT][4];
-    epi_stats<HT, KT, NW>(acc, mloc, my, nv, w, lane, scale_log2, red_m, red_s);
+    epi_stats<HT, KT, NW>(acc, mloc, my, nv, w, lane, a.scale_log2, red_m, red_s);
     __syncthreads();
-    {
-        const int h = 16 * ((lane >> 4) < HT ? (lane >> 4) : HT - 1) + (lane & 15);
-        const float nc = (nc_lse != nullptr && h < H) ? nc_lse[bt * H + h] : 0.f;
-        epi_rows<HT, KT, NW>(acc, mloc, m, my, w, lane, H, nc_lse != nullptr, nc, red_m, red_s, red_t);
-    }
+    epi_rows<HT, KT, NW>(acc, mloc, m, my, w, lane, H, FUSED || a.nc_lse != nullptr, nc, red_m, red_s, red_t);
     __syncthreads();
-    epi_scatter<KT, NW>(m, my, nv, w, lane, red_t, l1_floor, cslot, Tr);
+    epi_scatter<KT, NW>(m, my, nv, w, lane, red_t, a.l1_floor, cslot, Tr);
 }
 
-template <int DT, int HT, int KT, int NW>
-hipError_t launch3(const void *q, const void *pool, const int32_t *idx, const float *nc_lse, int B, int S, int H,
-                   int D, int N, int K, float scale, float l1_floor, float *target, hipStream_t stream) {
-    const size_t lds = (size_t)16 * HT * (D * Elem<DT>::bytes + 16) + (size_t)8 * K + (size_t)2 * NW * 16 * HT * 4 +
-                       (size_t)NW * 4 + (size_t)2 * NW * 4;
+template <int DT, int HT, int KT, int NW, bool FUSED>
+hipError_t launch3(const TargetArgs &a, hipStream_t stream) {
+    const size_t red = (size_t)NW * 16 * HT * 4;
+    const size_t lds = (size_t)16 * HT * (a.D * Elem<DT>::bytes + 16) + (size_t)8 * a.K + 2 * red + (size_t)NW * 4 +
+                       (size_t)2 * NW * 4 + (FUSED ? 2 * red : 0);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
-    const float fl = l1_floor > 0.f ? l1_floor : FLT_MIN;
-    auto kfn = &distill_target_kernel<DT, HT, KT, NW>;
+    auto kfn = &distill_target_kernel<DT, HT, KT, NW, FUSED>;
     if (lds > 65536) {  // opt in to more than 64 KiB of LDS per workgroup (gfx950 has 160 KiB per CU)
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kfn),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kfn, dim3((unsigned)((int64_t)B * S)), dim3(NW * 64), lds, stream, q, pool, idx, nc_lse, S, H,
-                       D, N, K, scale * kLog2e, fl, target);
+    hipLaunchKernelGGL(kfn, dim3((unsigned)((int64_t)a.B * a.S)), dim3(NW * 64), lds, stream, a);
     return hipGetLastError();
 }
 
-template <int DT, int HT>
-hipError_t launch2(const void *q, const void *pool, const int32_t *idx, const float *nc_lse, int B, int S, int H,
-                   int D, int N, int K, float scale, float l1_floor, float *target, hipStream_t stream) {
-#define SD_T(KT, NW) launch3<DT, HT, KT, NW>(q, pool, idx, nc_lse, B, S, H, D, N, K, scale, l1_floor, target, stream)
-    // K <= 16*NW*KT.
-    if (K <= 16) return SD_T(1, 1);
-    if (K <= 64) return SD_T(1, 4);
-    if (K <= 128) return SD_T(2, 4);
-    if (K <= 256) return SD_T(4, 4);
-    if (K <= 512) return SD_T(4, 8);
-    return SD_T(4, 16);
-#undef SD_T
+template <int DT, int HT, bool FUSED>
+hipError_t launch2(const TargetArgs &a, hipStream_t stream) {
+    const int K = a.K;
+    // K <= 16*NW*KT.  The fused form keeps NW >= 4 so each wave holds at most two of the
+    // (up to eight) window tiles.
+    if constexpr (!FUSED) {
+        if (K <= 16) return launch3<DT, HT, 1, 1, FUSED>(a, stream);
+    }
+    if (K <= 64) return launch3<DT, HT, 1, 4, FUSED>(a, stream);
+    if (K <= 128) return launch3<DT, HT, 2, 4, FUSED>(a, stream);
+    if (K <= 256) return launch3<DT, HT, 4, 4, FUSED>(a, stream);
+    if (K <= 512) return launch3<DT, HT, 4, 8, FUSED>(a, stream);
+    return launch3<DT, HT, 4, 16, FUSED>(a, stream);
 }
 
-template <int DT>
-hipError_t launch1(const void *q, const void *pool, const int32_t *idx, const float *nc_lse, int B, int S, int H,
-                   int D, int N, int K, float scale, float l1_floor, float *target, hipStream_t stream) {
-    if (H <= 16) return launch2<DT, 1>(q, pool, idx, nc_lse, B, S, H, D, N, K, scale, l1_floor, target, stream);
-    if (H <= 32) return launch2<DT, 2>(q, pool, idx, nc_lse, B, S, H, D, N, K, scale, l1_floor, target, stream);
-    return launch2<DT, 4>(q, pool, idx, nc_lse, B, S, H, D, N, K, scale, l1_floor, target, stream);
+template <int DT, bool FUSED>
+hipError_t launch1(const TargetArgs &a, hipStream_t stream) {
+    if (a.H <= 16) return launch2<DT, 1, FUSED>(a, stream);
+    if (a.H <= 32) return launch2<DT, 2, FUSED>(a, stream);
+    return launch2<DT, 4, FUSED>(a, stream);
+}
+
+template <bool FUSED>
+hipError_t launch0(TargetArgs a, float scale, float l1_floor, int dtype, hipStream_t stream) {
+    a.scale_log2 = scale * kLog2e;
+    a.l1_floor = l1_floor > 0.f ? l1_floor : FLT_MIN;
+    if (dtype == 0) return launch1<0, FUSED>(a, stream);
+    return launch1<1, FUSED>(a, stream);
 }
 
 }  // namespace
@@ -490,8 +604,23 @@ hipError_t launch1(const void *q, const void *pool, const int32_t *idx, const fl
 hipError_t launch_distill_target(const void *q, const void *pool, const int32_t *idx, const float *nc_lse,
                                  int B, int S, int H, int D, int N, int K, float scale, float l1_floor,
                                  int dtype, float *target, hipStream_t stream) {
-    if (dtype == 0) return launch1<0>(q, pool, idx, nc_lse, B, S, H, D, N, K, scale, l1_floor, target, stream);
-    return launch1<1>(q, pool, idx, nc_lse, B, S, H, D, N, K, scale, l1_floor, target, stream);
+    TargetArgs a{};
+    a.q = q; a.pool = pool; a.idx = idx; a.nc_lse = nc_lse;
+    a.B = B; a.S = S; a.H = H; a.D = D; a.N = N; a.K = K;
+    a.target = target;
+    return launch0<false>(a, scale, l1_floor, dtype, stream);
+}
+
+hipError_t launch_distill_target_fused(const void *q, const void *kwin, const float *sink, const int32_t *seg,
+                                       const void *pool, const int32_t *idx, int B, int S, int H, int D, int N,
+                                       int K, int W, float scale, float l1_floor, int dtype, float *target,
+                                       float *nc_out, hipStream_t stream) {
+    TargetArgs a{};
+    a.q = q; a.pool = pool; a.idx = idx;
+    a.kwin = kwin; a.sink = sink; a.seg = seg; a.nc_out = nc_out; a.W = W;
+    a.B = B; a.S = S; a.H = H; a.D = D; a.N = N; a.K = K;
+    a.target = target;
+    return launch0<true>(a, scale, l1_floor, dtype, stream);
 }
 
 }  // namespace sd

@@ -24,6 +24,11 @@ hipError_t launch_distill_target(const void *q, const void *pool, const int32_t 
                                  int B, int S, int H, int D, int N, int K, float scale, float l1_floor,
                                  int dtype, float *target, hipStream_t stream);
 
+hipError_t launch_distill_target_fused(const void *q, const void *kwin, const float *sink, const int32_t *seg,
+                                       const void *pool, const int32_t *idx, int B, int S, int H, int D, int N,
+                                       int K, int W, float scale, float l1_floor, int dtype, float *target,
+                                       float *nc_out, hipStream_t stream);
+
 size_t kl_workspace_bytes(int B, int S, int K);
 hipError_t launch_distill_kl(const float *target, const float *logits, const int32_t *idx, int B, int S,
                              int K, int N, float grad_scale, float *kl_rows, float *dlogits, float *stats,

@@ -31,10 +31,10 @@ def declared_functions():
     return sorted(set(re.findall(r"^[A-Za-z_][\w \t\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("window_lse", "distill_target", "distill_kl_fwd_bwd", "distill_kl_workspace_bytes",
-              "sd_status_string", "sd_last_error"):
+    for n in ("window_lse", "distill_target", "distill_target_fused", "distill_kl_fwd_bwd",
+              "distill_kl_workspace_bytes", "sd_status_string", "sd_last_error"):
         assert n in names, names
 
 
@@ -92,6 +92,31 @@ def test_distill_target_rejections(lib):
     assert _tg(lib, K=1025) == sd.SD_ERR_UNSUPPORTED
     assert _tg(lib, D=16) == sd.SD_ERR_UNSUPPORTED
     assert _tg(lib, H=128) == sd.SD_ERR_UNSUPPORTED
+
+
+def _tf(lib, q=FAKE, k=FAKE, pool=FAKE, idx=FAKE, out=FAKE, B=1, S=8, H=4, D=32, N=2, K=4, W=4, scale=0.1,
+        floor=0.0, dtype=0):
+    lib.distill_target_fused.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 7 + [ctypes.c_float] * 2 + \
+        [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    return lib.distill_target_fused(q, k, None, None, pool, idx, B, S, H, D, N, K, W, scale, floor, dtype, out,
+                                    None, None)
+
+
+def test_distill_target_fused_rejections(lib):
+    assert _tf(lib, q=None) == sd.SD_ERR_NULL_ARG
+    assert _tf(lib, k=None) == sd.SD_ERR_NULL_ARG
+    assert _tf(lib, pool=None) == sd.SD_ERR_NULL_ARG
+    assert _tf(lib, idx=None) == sd.SD_ERR_NULL_ARG
+    assert _tf(lib, out=None) == sd.SD_ERR_NULL_ARG
+    assert _tf(lib, W=0) == sd.SD_ERR_BAD_SHAPE
+    assert _tf(lib, N=0) == sd.SD_ERR_BAD_SHAPE
+    assert _tf(lib, scale=0.0) == sd.SD_ERR_BAD_SHAPE
+    assert _tf(lib, floor=float("nan")) == sd.SD_ERR_BAD_SHAPE
+    assert _tf(lib, dtype=7) == sd.SD_ERR_DTYPE
+    assert _tf(lib, W=129) == sd.SD_ERR_UNSUPPORTED
+    assert _tf(lib, K=1025) == sd.SD_ERR_UNSUPPORTED
+    assert _tf(lib, D=48) == sd.SD_ERR_UNSUPPORTED
+    assert b"head dim" in lib.sd_last_error()
 
 
 def _kl(lib, T=FAKE, z=FAKE, idx=FAKE, B=1, S=8, K=4, N=2, g=1.0, rows=FAKE, dz=FAKE, st=FAKE, ws=FAKE,

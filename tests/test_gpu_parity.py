@@ -91,7 +91,7 @@ def check_kl(kl_gpu, dz_gpu, kl_ref, dz_ref, idx_rows, N, what, T_rows, grad_sca
 
 
 # ------------------------------------------------------------------ the layer on a config
-def run_config(name, nsample=None, shuffle_pad=False):
+def run_config(name, nsample=None, shuffle_pad=False, fused=False):
     sd = _sd()
     x = synth.make_inputs(name, shuffle_pad=shuffle_pad)
     c = x["cfg"]
@@ -108,9 +108,9 @@ def run_config(name, nsample=None, shuffle_pad=False):
         z.reshape(-1, c.K)[torch.as_tensor(x["kl_zero_rows"])] = torch.from_numpy(zz)
     g = _to(x, dev)
     g["z"] = z.to(dev)
-    _say(f"[gpu] {name}: layer B={c.B} S={c.S} H={c.H} D={c.D} N={c.N} K={c.K} W={c.W} {c.dtype}")
+    _say(f"[gpu] {name}: layer B={c.B} S={c.S} H={c.H} D={c.D} N={c.N} K={c.K} W={c.W} {c.dtype} fused={fused}")
     out = sd.csa_distill_layer(g["q"], g["kwin"], g["pool"], g["idx"], g["z"], g["sink"], g["seg"], W=c.W,
-                               grad_scale=1.0)
+                               grad_scale=1.0, fused=fused)
     torch.cuda.synchronize()
     nc = _np(out["nc_lse"]).reshape(-1, c.H)[rows]
     T = _np(out["target"]).reshape(-1, c.K)[rows]
@@ -139,14 +139,18 @@ def run_config(name, nsample=None, shuffle_pad=False):
     return x, out, rows
 
 
+# fused=True runs distill_target_fused (window part inside the target kernel) instead of
+# window_lse + distill_target; the same oracle values check both.
+@pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
 @pytest.mark.parametrize("name", ["c1", "c2", "c1_local"])
-def test_layer_parity_all_rows(name):
-    run_config(name)
+def test_layer_parity_all_rows(name, fused):
+    run_config(name, fused=fused)
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
 @pytest.mark.parametrize("name", ["c3", "c4", "c3_local", "c5"])
-def test_layer_parity_full_size_sampled(name):
-    x, out, rows = run_config(name, nsample=48)
+def test_layer_parity_full_size_sampled(name, fused):
+    x, out, rows = run_config(name, nsample=48, fused=fused)
     c = x["cfg"]
     if len(x["kl_zero_rows"]):
         kl = _np(out["kl_rows"]).reshape(-1)[x["kl_zero_rows"]]
@@ -159,8 +163,9 @@ def test_layer_parity_full_size_sampled(name):
         np.testing.assert_allclose(T[ne].sum(-1), 1.0, atol=1e-4)
 
 
-def test_shuffled_padding_parity():
-    run_config("c2", shuffle_pad=True)
+@pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
+def test_shuffled_padding_parity(fused):
+    run_config("c2", shuffle_pad=True, fused=fused)
 
 
 # ------------------------------------------------------------------ isolated kernels
@@ -286,8 +291,9 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
 @pytest.mark.parametrize("case", EDGE, ids=lambda e: e[0])
-def test_edge_shapes(case):
+def test_edge_shapes(case, fused):
     name, B, S, H, D, N, K, W, dt, segs = case
     cid = 800 + EDGE.index(case)
     if segs > 1:
@@ -298,9 +304,9 @@ def test_edge_shapes(case):
     dev = _dev()
     x = synth.make_inputs(cfg, shuffle_pad=True)
     g = _to(x, dev)
-    _say(f"[gpu] edge {name}: B={B} S={S} H={H} D={D} N={N} K={K} W={W} {dt} segs={segs}")
+    _say(f"[gpu] edge {name}: B={B} S={S} H={H} D={D} N={N} K={K} W={W} {dt} segs={segs} fused={fused}")
     out = sd.csa_distill_layer(g["q"], g["kwin"], g["pool"], g["idx"], g["z"], g["sink"], g["seg"], W=W,
-                               grad_scale=1.0)
+                               grad_scale=1.0, fused=fused)
     torch.cuda.synchronize()
     nc_ref = oracle.window_lse(x["q"], x["kwin"], x["sink"], x["seg"], W, cfg.scale)
     T_ref = oracle.target(x["q"], x["pool"], x["idx"], x["kwin"], x["sink"], x["seg"], W=W, scale=cfg.scale)

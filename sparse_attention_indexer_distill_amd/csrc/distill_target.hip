@@ -117,7 +117,7 @@ __device__ __forceinline__ void score_tiles_q1(f32x4 (&acc)[KT][HT], const unsig
     };
     auto load_a = [&](u32x4(&a)[MY], int c) {
 #pragma unroll
-        for (int l = 0; l < MY; ++l) a[l] = buf_load16(pool, off[l] + (uint32_t)rot(c) * CB);
+        for (int l = 0; l < MY; ++l) a[l] = buf_load16_l2(pool, off[l] + (uint32_t)rot(c) * CB);
     };
     auto mma = [&](const u32x4(&a)[MY], int c) {
 #pragma unroll

@@ -78,17 +78,24 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
 }
 
+// Device-scope (sc1) load: served by L2 without allocating in the CU's L1.  Used for row
+// gathers, which have no L1 reuse and whose 1 KB-strided rows otherwise pile into a few L1
+// sets (tag-conflict stalls).
+__device__ __forceinline__ u32x4 buf_load16_l2(rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16 /* sc1 */);
+}
+
 // One fragment (8 elements) of a row at byte offset `byte_off`.
 template <int DT>
 __device__ __forceinline__ typename Elem<DT>::frag_t buf_load_frag(rsrc_t r, uint32_t byte_off);
 template <>
 __device__ __forceinline__ u32x4 buf_load_frag<0>(rsrc_t r, uint32_t byte_off) {
-    return buf_load16(r, byte_off);
+    return buf_load16_l2(r, byte_off);
 }
 template <>
 __device__ __forceinline__ f32x8 buf_load_frag<1>(rsrc_t r, uint32_t byte_off) {
-    const f32x4 lo = __builtin_bit_cast(f32x4, buf_load16(r, byte_off));
-    const f32x4 hi = __builtin_bit_cast(f32x4, buf_load16(r, byte_off + 16));
+    const f32x4 lo = __builtin_bit_cast(f32x4, buf_load16_l2(r, byte_off));
+    const f32x4 hi = __builtin_bit_cast(f32x4, buf_load16_l2(r, byte_off + 16));
     return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 

@@ -111,6 +111,21 @@ def cpu_baseline(cfg, x, kernels_s_per_layer: float) -> dict:
               x["idx"].reshape(-1, cfg.K).numpy()[rows], cfg.N)
     dt = time.perf_counter() - t0
     ms_layer = dt * 1e3 * (cfg.B * cfg.S) / len(rows)
+    # the same oracle on one core, over a smaller sample (every 64th row)
+    nthreads = oracle.num_threads()
+    rows1 = np.arange(0, cfg.B * cfg.S, 64)
+    oracle.set_num_threads(1)
+    try:
+        t1 = time.perf_counter()
+        oracle.window_lse(x["q"], x["kwin"], x["sink"], x["seg"], cfg.W, cfg.scale, rows=rows1)
+        T1 = oracle.target(x["q"], x["pool"], x["idx"], x["kwin"], x["sink"], x["seg"], W=cfg.W, scale=cfg.scale,
+                           rows=rows1)
+        oracle.kl(T1.astype(np.float32), x["z"].reshape(-1, cfg.K).numpy()[rows1],
+                  x["idx"].reshape(-1, cfg.K).numpy()[rows1], cfg.N)
+        dt1 = time.perf_counter() - t1
+    finally:
+        oracle.set_num_threads(nthreads)
+    ms_layer_1core = dt1 * 1e3 * (cfg.B * cfg.S) / len(rows1)
     cpu = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -119,7 +134,9 @@ def cpu_baseline(cfg, x, kernels_s_per_layer: float) -> dict:
                 break
     except OSError:
         pass
-    return {"value": round(ms_layer, 3), "unit": "ms", "cores": oracle.num_threads(), "kind": "oracle",
+    return {"value": round(ms_layer, 3), "unit": "ms", "cores": nthreads, "kind": "oracle",
+            "value_1core": round(ms_layer_1core, 3),
+            "sample_1core": f"{len(rows1)} rows (every 64th), {dt1:.2f} s wall on one thread",
             "sample": f"{len(rows)} of {cfg.B * cfg.S} rows (every 4th), fp64 window_lse + joint target + KL; "
                       f"{dt:.2f} s wall, scaled by {cfg.B * cfg.S / len(rows):.0f}x",
             "cpu": cpu, "nproc": os.cpu_count(), "gpu_speedup": round(ms_layer / (kernels_s_per_layer * 1e3), 1)}
@@ -134,6 +151,8 @@ def main() -> int:
     ap.add_argument("--path", default="3call", choices=["3call", "fused"],
                     help="3call: window_lse -> distill_target -> KL; fused: distill_target_fused -> KL")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--l2-cold", action="store_true",
+                    help="also time each kernel with L2 flushed before every step (512 MB touched, untimed)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB three times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -207,6 +226,18 @@ def main() -> int:
     torch.cuda.synchronize()
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
     per_min = {n: float(np.min([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    per_med = {n: float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    cold = None
+    if args.l2_cold:
+        # timed region 3 (reported separately): every step starts with a cold L2
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        evc = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            flush.fill_(i & 0xFF)
+            step(evc[i])
+        torch.cuda.synchronize()
+        cold = {n: round(float(np.median([e[j].elapsed_time(e[j + 1]) for e in evc])), 4) for j, n in enumerate(names)}
+        del flush
 
     work = algorithmic_work(cfg, x)
     kernels = {}
@@ -214,7 +245,8 @@ def main() -> int:
         ms = per[n]
         tf = work[n]["flops"] / (ms * 1e-3) / 1e12
         gbs = work[n]["bytes"] / (ms * 1e-3) / 1e9
-        kernels[n] = {"ms": round(ms, 4), "ms_min": round(per_min[n], 4), "TFLOP/s": round(tf, 1),
+        kernels[n] = {"ms": round(ms, 4), "ms_median": round(per_med[n], 4), "ms_min": round(per_min[n], 4),
+                      "TFLOP/s": round(tf, 1),
                       "GB/s": round(gbs, 1), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
                       "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
                       "algorithmic_flops": work[n]["flops"], "algorithmic_bytes": work[n]["bytes"],
@@ -234,6 +266,7 @@ def main() -> int:
         "roofline": roofline,
         "kernels": kernels,
         "path": args.path,
+        **({"l2_cold_ms_median": cold} if cold is not None else {}),
         "layer_useful_TFLOP/s": round(sum(work[n]["flops"] for n in names) / (ms_per_step * 1e-3) / 1e12, 1),
     }
     if not args.no_cpu_baseline:

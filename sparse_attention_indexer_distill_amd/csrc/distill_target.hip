@@ -73,7 +73,12 @@ __device__ __forceinline__ void score_tiles(f32x4 (&acc)[KT][HT], const unsigned
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) bq[ht] = q_frag<DT, HT>(qb, RS, ht, rot(c), lane);
     };
-    auto mma = [&](const frag_t(&a)[MY], const frag_t(&bq)[HT]) {
+    const int paddr = quad_to_frag_addr(lane);
+    auto mma = [&](frag_t(&a)[MY], const frag_t(&bq)[HT]) {
+        if constexpr (DT == 0) {  // bf16 rows were loaded quad-major
+#pragma unroll
+            for (int l = 0; l < MY; ++l) a[l] = quad_to_frag(a[l], paddr);
+        }
 #pragma unroll
         for (int l = 0; l < MY; ++l)
 #pragma unroll
@@ -119,7 +124,10 @@ __device__ __forceinline__ void score_tiles_q1(f32x4 (&acc)[KT][HT], const unsig
 #pragma unroll
         for (int l = 0; l < MY; ++l) a[l] = buf_load16_l2(pool, off[l] + (uint32_t)rot(c) * CB);
     };
-    auto mma = [&](const u32x4(&a)[MY], int c) {
+    const int paddr = quad_to_frag_addr(lane);
+    auto mma = [&](u32x4(&a)[MY], int c) {
+#pragma unroll
+        for (int l = 0; l < MY; ++l) a[l] = quad_to_frag(a[l], paddr);  // rows were loaded quad-major
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
             const u32x4 b = q_frag<0, HT>(qb, RS, ht, rot(c), lane);
@@ -404,9 +412,10 @@ __device__ __forceinline__ float window_part(const TargetArgs &a, const unsigned
         uint32_t off[KWT];
 #pragma unroll
         for (int l = 0; l < KWT; ++l) {
-            int r = kf + 16 * (w + l * NW) + (lane & 15);
+            int r = kf + 16 * (w + l * NW) + (DT == 0 ? (int)quad_row_lane(lane) : (lane & 15));
             r = r < t ? r : t;  // rows past t are loaded as row t and masked below
-            off[l] = (uint32_t)((r * D + 8 * (lane >> 4)) * EB);
+            off[l] = DT == 0 ? (uint32_t)(r * D * EB) + quad_seg_bytes(lane)
+                             : (uint32_t)((r * D + 8 * (lane >> 4)) * EB);
         }
         score_dispatch<DT, HT, KWT>(myw, acc, qb, RS, kr, off, nch, 0, lane);
     }
@@ -519,12 +528,15 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
         for (int h = 0; h < HT; ++h) acc[l][h] = f32x4{init, init, init, init};
     }
     {
+        // bf16: rows gathered quad-major (4 consecutive lanes per row, see sd_device.hpp);
+        // fp32: lane l on row l%16 (fragment layout)
         uint32_t off[KT];
 #pragma unroll
         for (int l = 0; l < KT; ++l) {
-            const int pos = 16 * (w + l * NW) + (lane & 15);
+            const int pos = 16 * (w + l * NW) + (DT == 0 ? (int)quad_row_lane(lane) : (lane & 15));
             const int r = (l < my && pos < nv) ? crow[pos] : crow[0];
-            off[l] = (uint32_t)((r * D + 8 * (lane >> 4)) * EB);
+            off[l] = DT == 0 ? (uint32_t)(r * D * EB) + quad_seg_bytes(lane)
+                             : (uint32_t)((r * D + 8 * (lane >> 4)) * EB);
         }
         // chunk rotation: even (keeps the chunk pairs of the pipelined loop), per wave and token
         const int cr = (nch & 1) ? 0 : (2 * (5 * w + (int)(bt % nch))) % nch;

@@ -119,6 +119,23 @@ __device__ __forceinline__ f32x8 lds_frag<1>(const u32x4 *units, int unit) {
     return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// ---- coalesced row gathers ---------------------------------------------------------
+// The memory pipeline merges the addresses of CONSECUTIVE lanes: a 16-row x 64-byte load
+// whose 4 consecutive lanes share a row streams at ~27 B/clk/CU on gfx950, but the
+// MFMA operand layout (lane l on row l%16) spreads each row over lanes 16 apart and runs
+// at ~15.5 B/clk/CU for the same bytes.  So rows are loaded "quad-major" -- lane L holds
+// row L/4, 16-byte segment L%4 of the chunk -- and moved into the fragment layout (lane
+// l: row l%16, segment l/16) with one ds_bpermute per dword (source lane 4*(l%16)+l/16).
+__device__ __forceinline__ uint32_t quad_row_lane(int lane) { return (uint32_t)(lane >> 2); }
+__device__ __forceinline__ uint32_t quad_seg_bytes(int lane) { return (uint32_t)(16 * (lane & 3)); }
+__device__ __forceinline__ int quad_to_frag_addr(int lane) { return (4 * (lane & 15) + (lane >> 4)) << 2; }
+__device__ __forceinline__ u32x4 quad_to_frag(u32x4 v, int addr) {
+    u32x4 r;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) r[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v[d]);
+    return r;
+}
+
 // ---- coalesced gather of 16-row operand tiles (bf16) ------------------------------
 // A 16x16x32 operand tile puts 4 lanes on each row (64 bytes of a row per load), which
 // costs one 128-byte L2 request per row and half-uses it.  Instead, the two chunks of a

@@ -29,18 +29,36 @@
 namespace sd {
 namespace {
 
-// Queries of one token in LDS: head row h at byte h*RS (RS = D*EB + 16: the 16-byte pad
-// makes the 16 rows of a fragment read fall in distinct banks).  A fragment unit for
-// (head tile ht, chunk c) is read at row 16*ht + l%16, byte (32c + 8*(l/16))*EB.
+// Queries of one token in LDS.
+// bf16: chunk-major -- the 16 heads x 32 elements of (chunk c, head tile ht) fill the 1 KB
+//   block c*HT + ht, head r of the tile at byte 64r, its four 16-byte groups rotated by
+//   qswz(r).  A fragment read (lane l: head l%16, group l/16) is then free of LDS bank
+//   conflicts, and blocks sit at constant offsets from one per-lane base.
+// fp32: head row h at byte h*RS (RS = D*4 + 16: the 16-byte pad puts the 16 rows of a
+//   fragment read in distinct banks); fragment unit (ht, c) at row 16*ht + l%16, byte
+//   (32c + 8*(l/16))*4.
 __device__ __forceinline__ int qrow_stride(int D, int EB) { return D * EB + 16; }
+__device__ __forceinline__ int qswz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int q_lane_bytes(int lane) {
+    const int r = lane & 15;
+    return 64 * r + 16 * ((lane >> 4) ^ qswz(r));
+}
+template <int HT>
+__device__ __forceinline__ int q_bytes(int DT, int D) {  // bf16: chunk count padded to even
+    return DT == 0 ? 1024 * HT * (((D >> 5) + 1) & ~1) : 16 * HT * qrow_stride(D, 4);
+}
+
+// bf16 fragment of block u (= c*HT + ht) from the lane's base address qb + q_lane_bytes.
+__device__ __forceinline__ u32x4 q_unit(const unsigned char *qlane, int u) {
+    return *reinterpret_cast<const u32x4 *>(qlane + (u << 10));
+}
 
 template <int DT, int HT>
 __device__ __forceinline__ typename Elem<DT>::frag_t q_frag(const unsigned char *qb, int RS, int ht, int c, int lane) {
-    constexpr int EB = Elem<DT>::bytes;
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(qb + (ht * 16 + (lane & 15)) * RS + (32 * c + 8 * (lane >> 4)) * EB);
     if constexpr (DT == 0) {
-        return p[0];
+        return q_unit(qb + q_lane_bytes(lane), c * HT + ht);
     } else {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(qb + (ht * 16 + (lane & 15)) * RS + (32 * c + 8 * (lane >> 4)) * 4);
         const f32x4 lo = __builtin_bit_cast(f32x4, p[0]), hi = __builtin_bit_cast(f32x4, p[1]);
         return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
@@ -108,60 +126,74 @@ __device__ __forceinline__ void score_tiles(f32x4 (&acc)[KT][HT], const unsigned
     mma(a1, b1);
 }
 
-// bf16 variant with only the pool fragments double-buffered: each query fragment is read
-// from LDS right before its MFMAs (the other waves of the SIMD cover the LDS latency),
-// which frees 4*HT registers per lane -- enough to keep the widest tile set spill-free.
-template <int HT, int MY, int KT>
-__device__ __forceinline__ void score_tiles_q1(f32x4 (&acc)[KT][HT], const unsigned char *__restrict__ qb, int RS,
-                                               rsrc_t pool, const uint32_t (&off)[KT], int nch, int cr, int lane) {
-    constexpr uint32_t CB = 64;  // bytes of one 32-element bf16 chunk of a row
-    u32x4 a0[MY], a1[MY];
-    auto rot = [&](int c) {
-        const int cc = c + cr;
-        return cc >= nch ? cc - nch : cc;
+// bf16 scores from 128-byte row pieces (two chunks per load pair; see pair_frags).  The
+// tiles are scored PT at a time, so only PT tiles' raw loads and fragments are live next
+// to the accumulators; the next piece's loads are issued as soon as the current one has
+// been permuted, and each query fragment is read from LDS once per chunk and pass.  With
+// an odd chunk count the last piece is half used (its upper 64 bytes belong to the next
+// row, or fall past the buffer end and read as zero).  cr rotates the piece order per
+// wave and token, which spreads the gathers over the L2 channels.
+template <int HT, int MY, int KT, int PT>
+__device__ __forceinline__ void score_pairs(f32x4 (&acc)[KT][HT], const unsigned char *__restrict__ qb,
+                                            rsrc_t pool, const uint32_t (&olo)[KT], const uint32_t (&ohi)[KT],
+                                            int nch, int cr, int lane) {
+    const int np = (nch + 1) >> 1;
+    const PairAddr pa = pair_frag_addr(lane);
+    const unsigned char *qlane = qb + q_lane_bytes(lane);
+    auto rot = [&](int p) {
+        const int pp = p + cr;
+        return pp >= np ? pp - np : pp;
     };
-    auto load_a = [&](u32x4(&a)[MY], int c) {
 #pragma unroll
-        for (int l = 0; l < MY; ++l) a[l] = buf_load16_l2(pool, off[l] + (uint32_t)rot(c) * CB);
-    };
-    const int paddr = quad_to_frag_addr(lane);
-    auto mma = [&](u32x4(&a)[MY], int c) {
+    for (int l0 = 0; l0 < MY; l0 += PT) {
+        u32x4 lo[PT], hi[PT];
+        auto load = [&](int p) {
+            const uint32_t pb = (uint32_t)rot(p) * 128u;
 #pragma unroll
-        for (int l = 0; l < MY; ++l) a[l] = quad_to_frag(a[l], paddr);  // rows were loaded quad-major
+            for (int t = 0; t < PT; ++t) {
+                if (l0 + t < MY) {
+                    lo[t] = buf_load16_l2(pool, olo[l0 + t] + pb);
+                    hi[t] = buf_load16_l2(pool, ohi[l0 + t] + pb);
+                }
+            }
+        };
+        load(0);
+        for (int p = 0; p < np; ++p) {
+            u32x4 f0[PT], f1[PT];
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-            const u32x4 b = q_frag<0, HT>(qb, RS, ht, rot(c), lane);
+            for (int t = 0; t < PT; ++t)
+                if (l0 + t < MY) pair_frags(lo[t], hi[t], f0[t], f1[t], pa);
+            const int c = 2 * rot(p);
+            if (p + 1 < np) load(p + 1);
+            if (c + 1 >= nch) {  // half piece: chunk c+1 is the zero padding chunk of the staged queries
 #pragma unroll
-            for (int l = 0; l < MY; ++l) acc[l][ht] = mfma_frag<0>(a[l], b, acc[l][ht]);
+                for (int t = 0; t < PT; ++t) f1[t] = u32x4{0u, 0u, 0u, 0u};
+            }
+            // 2*HT query blocks (c, 0..HT-1), (c+1, 0..HT-1) at consecutive KB; reads run two ahead
+            const unsigned char *qc = qlane + ((c * HT) << 10);
+            u32x4 bq[2];
+            bq[0] = q_unit(qc, 0);
+            bq[1] = q_unit(qc, 1);
+#pragma unroll
+            for (int u = 0; u < 2 * HT; ++u) {
+                const u32x4 b = bq[u & 1];
+                if (u + 2 < 2 * HT) bq[u & 1] = q_unit(qc, u + 2);
+#pragma unroll
+                for (int t = 0; t < PT; ++t)
+                    if (l0 + t < MY) acc[l0 + t][u % HT] = mfma_frag<0>(u < HT ? f0[t] : f1[t], b, acc[l0 + t][u % HT]);
+            }
         }
-    };
-    const int c0 = nch & 1;  // an odd chunk count runs its first chunk unpipelined
-    if (c0) {
-        load_a(a0, 0);
-        mma(a0, 0);
     }
-    if (c0 >= nch) return;
-    load_a(a0, c0);
-    int c = c0;
-    for (; c + 2 < nch; c += 2) {
-        load_a(a1, c + 1);
-        mma(a0, c);
-        load_a(a0, c + 2);
-        mma(a1, c + 1);
-    }
-    load_a(a1, c + 1);
-    mma(a0, c);
-    mma(a1, c + 1);
 }
 
-template <int HT, int KT, int MY = KT>
-__device__ __forceinline__ void score_dispatch_q1(int my, f32x4 (&acc)[KT][HT], const unsigned char *__restrict__ qb,
-                                                  int RS, rsrc_t pool, const uint32_t (&off)[KT], int nch, int cr,
-                                                  int lane) {
+template <int HT, int KT, int PT, int MY = KT>
+__device__ __forceinline__ void score_dispatch_pairs(int my, f32x4 (&acc)[KT][HT], const unsigned char *__restrict__ qb,
+                                                     rsrc_t pool, const uint32_t (&olo)[KT],
+                                                     const uint32_t (&ohi)[KT], int nch, int cr, int lane) {
     if (my == MY) {
-        score_tiles_q1<HT, MY, KT>(acc, qb, RS, pool, off, nch, cr, lane);
+        score_pairs<HT, MY, KT, PT>(acc, qb, pool, olo, ohi, nch, cr, lane);
     } else if constexpr (MY > 1) {
-        score_dispatch_q1<HT, KT, MY - 1>(my, acc, qb, RS, pool, off, nch, cr, lane);
+        score_dispatch_pairs<HT, KT, PT, MY - 1>(my, acc, qb, pool, olo, ohi, nch, cr, lane);
     }
 }
 
@@ -175,21 +207,34 @@ __device__ __forceinline__ void score_dispatch(int my, f32x4 (&acc)[KT][HT], con
     }
 }
 
-// Cooperative staging of a token's queries straight from HBM into LDS: each instruction
-// moves up to 1 KB of one head row (fully coalesced); heads >= H read as zero.  The loads
-// complete asynchronously (vmcnt); wait before reading.
+// Cooperative staging of a token's queries straight from HBM into LDS; heads >= H read as
+// zero.  bf16: one instruction per 1 KB block (chunk c, head tile ht) of the chunk-major
+// layout, 4 consecutive lanes on each head's 64 bytes.  fp32: each instruction moves up to
+// 1 KB of one head row.  The loads complete asynchronously (vmcnt); wait before reading.
 template <int DT, int HT, int NW>
 __device__ __forceinline__ void stage_queries(const void *q, int64_t bt, int H, int D, unsigned char *qb, int w,
                                               int lane) {
     constexpr int EB = Elem<DT>::bytes;
-    const int RS = qrow_stride(D, EB), rowb = D * EB;
-    const int npiece = (rowb + 1023) >> 10;
+    const int rowb = D * EB;
     const rsrc_t qr = make_rsrc(reinterpret_cast<const char *>(q) + (size_t)bt * H * D * EB, (uint32_t)(H * D * EB));
-    for (int u = w; u < 16 * HT * npiece; u += NW) {
-        const int h = u / npiece, o = (u - h * npiece) << 10;
-        if (o + 16 * lane < rowb) {
-            const uint32_t voff = h < H ? (uint32_t)(h * rowb + o + 16 * lane) : 0x80000000u;
-            buf_load_lds16(qr, qb + h * RS + o, voff);
+    if constexpr (DT == 0) {
+        const int r = lane >> 2;
+        const uint32_t lane_b = 16u * (uint32_t)((lane & 3) ^ qswz(r));
+        const int nch = D >> 5;
+        for (int u = w; u < ((nch + 1) & ~1) * HT; u += NW) {  // odd nch: one zero chunk of padding
+            const int c = u / HT, h = 16 * (u - c * HT) + r;
+            const uint32_t voff = h < H && c < nch ? (uint32_t)(h * rowb + 64 * c) + lane_b : 0x80000000u;
+            buf_load_lds16(qr, qb + (u << 10), voff);
+        }
+    } else {
+        const int RS = qrow_stride(D, EB);
+        const int npiece = (rowb + 1023) >> 10;
+        for (int u = w; u < 16 * HT * npiece; u += NW) {
+            const int h = u / npiece, o = (u - h * npiece) << 10;
+            if (o + 16 * lane < rowb) {
+                const uint32_t voff = h < H ? (uint32_t)(h * rowb + o + 16 * lane) : 0x80000000u;
+                buf_load_lds16(qr, qb + h * RS + o, voff);
+            }
         }
     }
 }
@@ -479,8 +524,8 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
     const int S = a.S, H = a.H, D = a.D, N = a.N, K = a.K;
     const int nch = D >> 5;
     const int RS = qrow_stride(D, EB);
-    unsigned char *qb = smem;                                                  // [16*HT rows][RS bytes]
-    int32_t *crow = reinterpret_cast<int32_t *>(smem + 16 * HT * RS);         // [K] pool row per compacted slot
+    unsigned char *qb = smem;                                                  // the token's queries
+    int32_t *crow = reinterpret_cast<int32_t *>(smem + q_bytes<HT>(DT, D));   // [K] pool row per compacted slot
     int32_t *cslot = crow + K;                                                // [K] slot index per compacted slot
     float *red_m = reinterpret_cast<float *>(cslot + K);                      // [NW][16][HT] per-wave head max
     float *red_s = red_m + NW * 16 * HT;                                      // [NW][16][HT] per-wave head sum
@@ -527,25 +572,31 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
 #pragma unroll
         for (int h = 0; h < HT; ++h) acc[l][h] = f32x4{init, init, init, init};
     }
-    {
-        // bf16: rows gathered quad-major (4 consecutive lanes per row, see sd_device.hpp);
+    if constexpr (DT == 0) {
+        // bf16: 128-byte row pieces, lanes 8 to a row (see pair_frags)
+        uint32_t olo[KT], ohi[KT];
+#pragma unroll
+        for (int l = 0; l < KT; ++l) {
+            const int pos = 16 * (w + l * NW) + pair_row_lane(lane);
+            const int r0 = (l < my && pos < nv) ? crow[pos] : crow[0];
+            const int r1 = (l < my && pos + 8 < nv) ? crow[pos + 8] : crow[0];
+            olo[l] = (uint32_t)(r0 * D * EB) + pair_seg_bytes(lane);
+            ohi[l] = (uint32_t)(r1 * D * EB) + pair_seg_bytes(lane);
+        }
+        constexpr int PT = KT * HT >= 16 ? 2 : KT;  // tiles per pass: 2 at the widest tile set
+        const int np = (nch + 1) >> 1;
+        const int cr = (5 * w + (int)(bt % np)) % np;
+        if (my > 0) score_dispatch_pairs<HT, KT, PT>(my, acc, qb, pr, olo, ohi, nch, cr, lane);
+    } else {
         // fp32: lane l on row l%16 (fragment layout)
         uint32_t off[KT];
 #pragma unroll
         for (int l = 0; l < KT; ++l) {
-            const int pos = 16 * (w + l * NW) + (DT == 0 ? (int)quad_row_lane(lane) : (lane & 15));
+            const int pos = 16 * (w + l * NW) + (lane & 15);
             const int r = (l < my && pos < nv) ? crow[pos] : crow[0];
-            off[l] = DT == 0 ? (uint32_t)(r * D * EB) + quad_seg_bytes(lane)
-                             : (uint32_t)((r * D + 8 * (lane >> 4)) * EB);
+            off[l] = (uint32_t)((r * D + 8 * (lane >> 4)) * EB);
         }
-        // chunk rotation: even (keeps the chunk pairs of the pipelined loop), per wave and token
-        const int cr = (nch & 1) ? 0 : (2 * (5 * w + (int)(bt % nch))) % nch;
-        if (my > 0) {
-            if constexpr (DT == 0 && KT * HT >= 16)
-                score_dispatch_q1<HT, KT>(my, acc, qb, RS, pr, off, nch, cr, lane);
-            else
-                score_dispatch<DT, HT, KT>(my, acc, qb, RS, pr, off, nch, cr, lane);
-        }
+        if (my > 0) score_dispatch<DT, HT, KT>(my, acc, qb, RS, pr, off, nch, 0, lane);
     }
 
     // 3.-6. Epilogue: per-head statistics, joint denominators, head sums, normalised scatter.
@@ -568,7 +619,8 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
 template <int DT, int HT, int KT, int NW, bool FUSED>
 hipError_t launch3(const TargetArgs &a, hipStream_t stream) {
     const size_t red = (size_t)NW * 16 * HT * 4;
-    const size_t lds = (size_t)16 * HT * (a.D * Elem<DT>::bytes + 16) + (size_t)8 * a.K + 2 * red + (size_t)NW * 4 +
+    const size_t qbytes = DT == 0 ? (size_t)1024 * HT * (((a.D >> 5) + 1) & ~1) : (size_t)16 * HT * (a.D * 4 + 16);
+    const size_t lds = qbytes + (size_t)8 * a.K + 2 * red + (size_t)NW * 4 +
                        (size_t)2 * NW * 4 + (FUSED ? 2 * red : 0);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     auto kfn = &distill_target_kernel<DT, HT, KT, NW, FUSED>;

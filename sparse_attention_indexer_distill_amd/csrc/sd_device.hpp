@@ -124,11 +124,16 @@ __device__ __forceinline__ f32x8 lds_frag<1>(const u32x4 *units, int unit) {
 // whose 4 consecutive lanes share a row streams at ~27 B/clk/CU on gfx950, but the
 // MFMA operand layout (lane l on row l%16) spreads each row over lanes 16 apart and runs
 // at ~15.5 B/clk/CU for the same bytes.  So rows are loaded "quad-major" -- lane L holds
-// row L/4, 16-byte segment L%4 of the chunk -- and moved into the fragment layout (lane
-// l: row l%16, segment l/16) with one ds_bpermute per dword (source lane 4*(l%16)+l/16).
+// row L/4 -- and moved into the fragment layout (lane l: row l%16, segment l/16) with one
+// ds_bpermute per dword.  Within a quad the upper half-wave (rows 8..15) takes the four
+// segments in the order 2,3,0,1: the permute's source lanes, 4*(l%16) + ((l/16) ^ 2*(row
+// >= 8)), are then distinct modulo 32 in each half-wave, which keeps the permute free of
+// LDS bank conflicts (the plain order 4*(l%16) + l/16 hits every bank twice).
 __device__ __forceinline__ uint32_t quad_row_lane(int lane) { return (uint32_t)(lane >> 2); }
-__device__ __forceinline__ uint32_t quad_seg_bytes(int lane) { return (uint32_t)(16 * (lane & 3)); }
-__device__ __forceinline__ int quad_to_frag_addr(int lane) { return (4 * (lane & 15) + (lane >> 4)) << 2; }
+__device__ __forceinline__ uint32_t quad_seg_bytes(int lane) { return (uint32_t)(16 * ((lane & 3) ^ ((lane >> 4) & 2))); }
+__device__ __forceinline__ int quad_to_frag_addr(int lane) {
+    return (4 * (lane & 15) + ((lane >> 4) ^ ((lane >> 2) & 2))) << 2;
+}
 __device__ __forceinline__ u32x4 quad_to_frag(u32x4 v, int addr) {
     u32x4 r;
 #pragma unroll
@@ -136,30 +141,40 @@ __device__ __forceinline__ u32x4 quad_to_frag(u32x4 v, int addr) {
     return r;
 }
 
-// ---- coalesced gather of 16-row operand tiles (bf16) ------------------------------
-// A 16x16x32 operand tile puts 4 lanes on each row (64 bytes of a row per load), which
-// costs one 128-byte L2 request per row and half-uses it.  Instead, the two chunks of a
-// 128-byte line (chunks 2p and 2p+1) of a 16-row tile are fetched with two loads that
-// each cover 8 rows x 128 bytes:
-//     load lo: lane (r = l/16, x = l%16) holds row x%8,     16-byte segment r + 4*(x/8)
-//     load hi: lane (r, x)               holds row 8 + x%8, segment r + 4*(x/8)
-// The fragment of chunk 2p (segments 0..3) is lo for x < 8 and hi rotated by 8 lanes
-// within the 16-lane row for x >= 8; chunk 2p+1 (segments 4..7) is lo rotated by 8 for
-// x < 8 and hi for x >= 8.  Byte offset of a lane's segment inside the line:
-__device__ __forceinline__ uint32_t pair_seg_bytes(int lane) { return (uint32_t)(16 * ((lane >> 4) + 4 * ((lane >> 3) & 1))); }
+// ---- 128-byte row pieces (bf16) -------------------------------------------------------
+// With 8 consecutive lanes on a row, one load covers 8 rows x 128 bytes (two 32-element
+// chunks, 2p and 2p+1) and streams at ~48 B/clk/CU, against ~27 for 16 rows x 64 bytes.
+// A 16-row tile takes two such loads:
+//     lo: lane L holds row L/8,     16-byte segment s(L) of the piece
+//     hi: lane L holds row 8 + L/8, segment s(L)
+// with s(L) = (L%8) ^ 2*(L >= 32): the upper half-wave takes its segments in the order
+// 2,3,0,1,6,7,4,5, which keeps the permute below free of LDS bank conflicts (the lanes of
+// a row still cover one 128-byte line, so the load coalesces the same).
+__device__ __forceinline__ int pair_row_lane(int lane) { return lane >> 3; }
+__device__ __forceinline__ uint32_t pair_seg_bytes(int lane) { return (uint32_t)(16 * ((lane & 7) ^ ((lane >> 4) & 2))); }
 
-// In place: lo becomes the fragment of chunk 2p, hi the fragment of chunk 2p+1
-// (low_half: lane%16 < 8).  row_ror:8 never leaves the 16-lane row, so bound_ctrl
-// costs nothing and spares the move of an "old" value: two VALU ops per dword.
-__device__ __forceinline__ uint32_t ror8(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, true);  // row_ror:8
+// Fragments of chunk 2p (f0) and chunk 2p+1 (f1) from the two loads of a tile.  A
+// bank-masked row shift first gathers each chunk into one register,
+//     A = lo on lanes L%8 < 4, hi from lane L-4 on the others   (chunk 2p, all 16 rows)
+//     B = hi from lane L+4 on lanes L%8 < 4, lo on the others   (chunk 2p+1)
+// then one ds_bpermute per dword moves (row r, segment g) to fragment lane 16g + r.
+// Source lanes (r8 = r%8, hb = r/8, x = 2*(r8 >= 4)):
+//     f0: 8*r8 + 4*hb + (g ^ x)        f1: 8*r8 + 4*(1-hb) + (g ^ x)
+struct PairAddr {
+    int a0, a1;  // byte addresses for ds_bpermute
+};
+__device__ __forceinline__ PairAddr pair_frag_addr(int lane) {
+    const int r = lane & 15, g = lane >> 4, r8 = r & 7, hb = r >> 3, gx = g ^ (2 * (r8 >> 2));
+    return PairAddr{(8 * r8 + 4 * hb + gx) << 2, (8 * r8 + 4 * (1 - hb) + gx) << 2};
 }
-__device__ __forceinline__ void pair_to_frags(u32x4 &lo, u32x4 &hi, bool low_half) {
+__device__ __forceinline__ void pair_frags(const u32x4 &lo, const u32x4 &hi, u32x4 &f0, u32x4 &f1, PairAddr pa) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const uint32_t rl = ror8(lo[v]), rh = ror8(hi[v]);
-        lo[v] = low_half ? lo[v] : rh;
-        hi[v] = low_half ? rl : hi[v];
+    for (int d = 0; d < 4; ++d) {
+        // row_shr:4 (source lane L-4) into banks 1,3; row_shl:4 (source L+4) into banks 0,2
+        const int A = __builtin_amdgcn_update_dpp((int)lo[d], (int)hi[d], 0x114, 0xf, 0xa, false);
+        const int B = __builtin_amdgcn_update_dpp((int)lo[d], (int)hi[d], 0x104, 0xf, 0x5, false);
+        f0[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(pa.a0, A);
+        f1[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(pa.a1, B);
     }
 }
 

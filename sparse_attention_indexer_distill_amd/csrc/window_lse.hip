@@ -155,7 +155,8 @@ __global__ __launch_bounds__(kWinTok * 64) void window_lse_kernel(
 // rows x 128 bytes (fully coalesced):
 //   * the key band its tokens span (16-key tiles covering [t0-W+1, t0+3]; from L2),
 //     double buffered, one stage ahead;
-//   * the queries of its 4 tokens (from HBM), triple buffered, two stages ahead.
+//   * the queries of its 4 tokens (from HBM), triple buffered, two stages ahead; each
+//     wave's two query loads of a stage are issued between its MFMAs.
 // Rows are stored with their 16-byte segments XOR-swizzled by (row >> 1) & 7, so the
 // 16-row MFMA fragment reads hit distinct LDS banks.  Loads retire in order, so each
 // stage ends with a counted wait that leaves only the farthest query stage in flight.
@@ -208,15 +209,20 @@ __global__ __launch_bounds__(1024) void window_lse_mfma_kernel(
         }
     };
     // Queries of D stage st into query buffer st%3; row = tok*HP + head.
-    auto stage_q = [&](int st) {
+    // Each wave issues exactly two of the TOK*HP/8 = 8*HG instructions (8*HG / (4*HG)
+    // waves): k = 0, 1.
+    auto stage_q_one = [&](int st, int k) {
         unsigned char *dst = qst + (st % 3) * qst_bytes;
-        for (int m = w; m < kTokMfma * HP / 8; m += nwaves) {
-            const int r = 8 * m + r_in;
-            const int x = (lane & 7) ^ ((r >> 1) & 7);
-            const int tk = r / HP, hd = r - tk * HP;
-            const uint32_t voff = hd < H ? (uint32_t)(((tk * H + hd) * D + st * 64 + 8 * x) * 2) : 0x80000000u;
-            buf_load_lds16(qr, dst + m * 1024, voff);
-        }
+        const int m = w + k * nwaves;
+        const int r = 8 * m + r_in;
+        const int x = (lane & 7) ^ ((r >> 1) & 7);
+        const int tk = r / HP, hd = r - tk * HP;
+        const uint32_t voff = hd < H ? (uint32_t)(((tk * H + hd) * D + st * 64 + 8 * x) * 2) : 0x80000000u;
+        buf_load_lds16(qr, dst + m * 1024, voff);
+    };
+    auto stage_q = [&](int st) {
+        stage_q_one(st, 0);
+        stage_q_one(st, 1);
     };
     if (seg) {
         for (int i = tid; i < nb * 16; i += blockDim.x) {
@@ -238,7 +244,10 @@ __global__ __launch_bounds__(1024) void window_lse_mfma_kernel(
     // at a fixed base plus 2048*j bytes (an immediate offset).
     const int rq = tok * HP + hg * 16 + (lane & 15);
     const int rb = wfirst * 16 + (lane & 15);
-    auto compute = [&](int st) {
+    // MFMAs of stage st.  With qst_next >= 0 the wave's two query loads of that stage are
+    // issued in the middle of the two chunks' MFMA runs, so the workgroup's loads reach the
+    // memory pipeline spread over the stage instead of as one burst after the barrier.
+    auto compute = [&](int st, int qst_next) {
         const unsigned char *bsrc = band + (st & 1) * band_bytes;
         const unsigned char *qsrc = qst + (st % 3) * qst_bytes;
 #pragma unroll
@@ -249,6 +258,11 @@ __global__ __launch_bounds__(1024) void window_lse_mfma_kernel(
             u32x4 a = *reinterpret_cast<const u32x4 *>(fb);
 #pragma unroll
             for (int j = 0; j < NBT; ++j) {
+                if (j == NBT / 2 && qst_next >= 0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    stage_q_one(qst_next, c);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 u32x4 an = a;
                 if (j + 1 < NBT) an = *reinterpret_cast<const u32x4 *>(fb + 2048 * (j + 1));
                 acc[j] = mfma_frag<0>(a, bq, acc[j]);
@@ -258,8 +272,6 @@ __global__ __launch_bounds__(1024) void window_lse_mfma_kernel(
     };
 
     const int nst = D >> 6;
-    // my far query loads per stage (the wave's share of the TOK*HP/8 instructions)
-    const int nfar = (kTokMfma * HP / 8 - w + nwaves - 1) / nwaves;
     stage_q(0);
     if (nst > 1) stage_q(1);
     stage_band(0);
@@ -268,16 +280,18 @@ __global__ __launch_bounds__(1024) void window_lse_mfma_kernel(
     for (int st = 0; st < nst; ++st) {
         if (st + 1 < nst) stage_band(st + 1);
         const bool far = st + 2 < nst;
-        if (far) stage_q(st + 2);
-        compute(st);
-        if (far && nfar > 0) {
-            // wait for everything but this wave's nfar (<= 2) far query loads
-            if (nfar == 1) __builtin_amdgcn_s_waitcnt((1 & 0xF) | (0x7 << 4) | (0xF << 8));
-            else __builtin_amdgcn_s_waitcnt((2 & 0xF) | (0x7 << 4) | (0xF << 8));
+        compute(st, far ? st + 2 : -1);  // issues the far query stage (after the band loads)
+        if (far) {
+            // wait for everything but this wave's two far query loads
+            __builtin_amdgcn_s_waitcnt((2 & 0xF) | (0x7 << 4) | (0xF << 8));
         } else {
             __builtin_amdgcn_s_waitcnt(0);
         }
-        __syncthreads();
+        // A plain s_barrier: the counted wait above has landed this wave's share of the next
+        // stage, and its LDS reads of this stage were consumed by its MFMAs.  (__syncthreads
+        // adds a workgroup release fence, i.e. vmcnt(0), which would also drain the far
+        // query stage.)
+        __builtin_amdgcn_s_barrier();
     }
     if (!active) return;
 

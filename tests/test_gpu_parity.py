@@ -283,8 +283,7 @@ EDGE = [
     ("all_empty", 1, 3, 4, 32, 4, 4, 2, "f32", 1),
     ("f32_h64", 1, 48, 64, 128, 12, 40, 33, "f32", 1),
     ("k_gt_blocks", 2, 44, 8, 32, 11, 300, 20, "bf16", 1),
-    # D = 512 bf16 with >= 2 tokens per CU: the persistent multi-token target kernel
-    # (XCD-split token order for B = 2, plain order for B = 3; 1, 2 and 4 head tiles)
+    # D = 512 bf16 with several tokens per CU: 1, 2 and 4 head tiles, 2 and 3 batch rows
     ("persist_b2_h20", 2, 600, 20, 512, 150, 300, 33, "bf16", 1),
     ("persist_b3_h64", 3, 400, 64, 512, 100, 512, 64, "bf16", 2),
     ("persist_k16_h5", 1, 1024, 5, 512, 256, 16, 40, "bf16", 1),

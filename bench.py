@@ -151,6 +151,8 @@ def main() -> int:
     ap.add_argument("--path", default="3call", choices=["3call", "fused"],
                     help="3call: window_lse -> distill_target -> KL; fused: distill_target_fused -> KL")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time whole steps as replays of one captured HIP graph of the step")
     ap.add_argument("--l2-cold", action="store_true",
                     help="also time each kernel with L2 flushed before every step (512 MB touched, untimed)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -212,10 +214,33 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        # one step captured as a HIP graph (the library only launches kernels on the
+        # capturing stream: no allocation, copy or memset inside the step)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        # the replay must reproduce the eager step bit for bit (every reduction has a fixed order)
+        outs = ("nc_lse", "target", "kl_rows", "dlogits", "stats")
+        step()
+        torch.cuda.synchronize()
+        ref = {k: bufs[k].clone() for k in outs}
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in outs:
+            if not torch.equal(bufs[k], ref[k]):
+                raise SystemExit(f"bench: graph replay differs from the eager step in {k}")
     # timed region 1: whole steps, wall clock between device synchronisations
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     # timed region 2: the same steps with HIP events between the kernels (per-kernel time)
@@ -266,6 +291,7 @@ def main() -> int:
         "roofline": roofline,
         "kernels": kernels,
         "path": args.path,
+        "timing": "graph replay" if args.graph else "eager launches",
         **({"l2_cold_ms_median": cold} if cold is not None else {}),
         "layer_useful_TFLOP/s": round(sum(work[n]["flops"] for n in names) / (ms_per_step * 1e-3) / 1e12, 1),
     }

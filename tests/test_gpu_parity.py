@@ -383,6 +383,45 @@ def test_deterministic_bitwise():
         assert torch.equal(a[k], b[k]), k
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
+def test_graph_capture_replays_match_eager(fused):
+    """A layer step captured as a HIP graph replays bit-identically to the eager step, on
+    every replay, with other eager work (a different layer into other buffers) between
+    the replays.  Every kernel reduction has a fixed order, so equality is exact."""
+    sd = _sd()
+    dev = _dev()
+    x = synth.make_inputs("c2")
+    c = x["cfg"]
+    g = _to(x, dev)
+    B, S, H, K = c.B, c.S, c.H, c.K
+
+    def new_bufs():
+        return dict(nc_lse=torch.empty(B, S, H, device=dev), target=torch.empty(B, S, K, device=dev),
+                    kl_rows=torch.empty(B, S, device=dev), dlogits=torch.empty(B, S, K, device=dev),
+                    stats=torch.empty(2, device=dev),
+                    workspace=torch.empty(sd.distill_kl_workspace_bytes(B, S, K), dtype=torch.uint8, device=dev))
+
+    bufs, other = new_bufs(), new_bufs()
+    run = lambda bb, z: sd.csa_distill_layer(g["q"], g["kwin"], g["pool"], g["idx"], z, g["sink"], g["seg"],
+                                             W=c.W, grad_scale=0.5, fused=fused, bufs=bb)
+    _say(f"[gpu] c2: graph capture ({'fused' if fused else '3call'})")
+    ref = {k: v.clone() for k, v in run(bufs, g["z"]).items()}
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(bufs, g["z"])
+    z2 = g["z"] * 1.5 + 0.25
+    for rep in range(3):
+        for v in bufs.values():
+            v.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(bufs[k], ref[k]), (rep, k)
+        run(other, z2)  # eager work between the replays
+        torch.cuda.synchronize()
+
+
 def test_binding_rejects_bad_arguments_on_gpu_tensors():
     sd = _sd()
     dev = _dev()

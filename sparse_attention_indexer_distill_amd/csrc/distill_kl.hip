@@ -150,35 +150,34 @@ __global__ __launch_bounds__(kKlRowsPerBlock * 64) void distill_kl_kernel(
     }
 }
 
-// Adds the per-block partials in a fixed order (one block).
+// Adds the per-block partials in a fixed order (one block of 4 waves): each thread sums a
+// strided set of 16-byte (sum, count, sum, count) loads in order, each wave reduces with
+// a fixed xor butterfly, and wave 0 adds the 4 wave totals after the single barrier.
 __global__ __launch_bounds__(256) void distill_kl_finalize(const float *__restrict__ partials, int nblk,
                                                            float *__restrict__ stats) {
-    __shared__ float ss[256], sc[256];
+    __shared__ float ws[4], wc[4];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     float s = 0.f, c = 0.f;
-    // partials are 8-byte aligned (sum, count) pairs: read two per 16-byte load
-    const int npair2 = nblk >> 1;
-    for (int i = threadIdx.x; i < npair2; i += 256) {
+    const int npair2 = nblk >> 1;  // partials are 8-byte aligned pairs: two per 16-byte load
+    for (int i = tid; i < npair2; i += 256) {
         const f32x4 v = reinterpret_cast<const f32x4 *>(partials)[i];
         s += v[0] + v[2];
         c += v[1] + v[3];
     }
-    if ((nblk & 1) && threadIdx.x == 0) {
+    if ((nblk & 1) && tid == 0) {
         s += partials[2 * (size_t)(nblk - 1)];
         c += partials[2 * (size_t)(nblk - 1) + 1];
     }
-    ss[threadIdx.x] = s;
-    sc[threadIdx.x] = c;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if ((int)threadIdx.x < o) {
-            ss[threadIdx.x] += ss[threadIdx.x + o];
-            sc[threadIdx.x] += sc[threadIdx.x + o];
-        }
-        __syncthreads();
+    s = wave_sum(s);
+    c = wave_sum(c);
+    if (lane == 0) {
+        ws[w] = s;
+        wc[w] = c;
     }
-    if (threadIdx.x == 0) {
-        stats[0] = ss[0];
-        stats[1] = sc[0];
+    __syncthreads();
+    if (tid == 0) {
+        stats[0] = (ws[0] + ws[1]) + (ws[2] + ws[3]);
+        stats[1] = (wc[0] + wc[1]) + (wc[2] + wc[3]);
     }
 }
 

@@ -43,7 +43,9 @@ KERNEL_SOURCES = {
 
 def src_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for p in (KERNEL_SOURCES[kernel], "sparse_attention_indexer_distill_amd/csrc/sd_device.hpp"):
+    # the kernel's source, the shared device header and the build flags
+    for p in (KERNEL_SOURCES[kernel], "sparse_attention_indexer_distill_amd/csrc/sd_device.hpp",
+              "sparse_attention_indexer_distill_amd/build.py"):
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
 

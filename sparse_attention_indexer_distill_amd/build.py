@@ -26,9 +26,15 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          f"-I{os.path.join(ROOT, 'include')}"]
 
 
+# Per-file scheduler choice: the target kernel's score loop is bound by LDS traffic, and
+# LLVM's memory-clause strategy (groups its loads) measured 2% faster on it than the
+# default occupancy-driven one.
+FILE_FLAGS = {"distill_target.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

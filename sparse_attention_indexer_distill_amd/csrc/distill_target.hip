@@ -30,33 +30,34 @@ namespace sd {
 namespace {
 
 // Queries of one token in LDS.
-// bf16: chunk-major -- the 16 heads x 32 elements of (chunk c, head tile ht) fill the 1 KB
-//   block c*HT + ht, head r of the tile at byte 64r, its four 16-byte groups rotated by
-//   qswz(r).  A fragment read (lane l: head l%16, group l/16) is then free of LDS bank
-//   conflicts, and blocks sit at constant offsets from one per-lane base.
-// fp32: head row h at byte h*RS (RS = D*4 + 16: the 16-byte pad puts the 16 rows of a
-//   fragment read in distinct banks); fragment unit (ht, c) at row 16*ht + l%16, byte
-//   (32c + 8*(l/16))*4.
+// bf16: pair-major -- the 16 heads x 64 elements of (chunk pair p, head tile ht) fill the
+//   2 KB block p*HT + ht; head r of the tile owns the 128 bytes at 128r, holding its eight
+//   16-byte segments x (chunk 2p: x = 0..3, chunk 2p+1: x = 4..7) at slot x ^ ((r>>1)&7).
+//   A fragment read (lane l: head l%16, segment 4*(c%2) + l/16) is then free of LDS bank
+//   conflicts (measured; the 64-byte-row layouts tried before paid 4 extra cycles per
+//   read), and all blocks sit at constant offsets from two per-lane bases (one per chunk
+//   parity).  An odd chunk count stages a zero chunk to complete the last pair.
+// fp32: head row h at byte h*RS (RS = D*4 + 16); fragment unit (ht, c) at row
+//   16*ht + l%16, byte (32c + 8*(l/16))*4.
 __device__ __forceinline__ int qrow_stride(int D, int EB) { return D * EB + 16; }
-__device__ __forceinline__ int qswz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-__device__ __forceinline__ int q_lane_bytes(int lane) {
+__device__ __forceinline__ int q_lane_bytes(int lane, int parity) {
     const int r = lane & 15;
-    return 64 * r + 16 * ((lane >> 4) ^ qswz(r));
+    return 128 * r + 16 * ((4 * parity + (lane >> 4)) ^ ((r >> 1) & 7));
 }
 template <int HT>
-__device__ __forceinline__ int q_bytes(int DT, int D) {  // bf16: chunk count padded to even
-    return DT == 0 ? 1024 * HT * (((D >> 5) + 1) & ~1) : 16 * HT * qrow_stride(D, 4);
+__device__ __forceinline__ int q_bytes(int DT, int D) {
+    return DT == 0 ? 2048 * HT * (((D >> 5) + 1) >> 1) : 16 * HT * qrow_stride(D, 4);
 }
 
-// bf16 fragment of block u (= c*HT + ht) from the lane's base address qb + q_lane_bytes.
+// bf16 fragment of block u (= pair*HT + ht) from a lane base qb + q_lane_bytes(lane, parity).
 __device__ __forceinline__ u32x4 q_unit(const unsigned char *qlane, int u) {
-    return *reinterpret_cast<const u32x4 *>(qlane + (u << 10));
+    return *reinterpret_cast<const u32x4 *>(qlane + (u << 11));
 }
 
 template <int DT, int HT>
 __device__ __forceinline__ typename Elem<DT>::frag_t q_frag(const unsigned char *qb, int RS, int ht, int c, int lane) {
     if constexpr (DT == 0) {
-        return q_unit(qb + q_lane_bytes(lane), c * HT + ht);
+        return q_unit(qb + q_lane_bytes(lane, c & 1), (c >> 1) * HT + ht);
     } else {
         const u32x4 *p = reinterpret_cast<const u32x4 *>(qb + (ht * 16 + (lane & 15)) * RS + (32 * c + 8 * (lane >> 4)) * 4);
         const f32x4 lo = __builtin_bit_cast(f32x4, p[0]), hi = __builtin_bit_cast(f32x4, p[1]);
@@ -139,7 +140,7 @@ __device__ __forceinline__ void score_pairs(f32x4 (&acc)[KT][HT], const unsigned
                                             int nch, int cr, int lane) {
     const int np = (nch + 1) >> 1;
     const PairAddr pa = pair_frag_addr(lane);
-    const unsigned char *qlane = qb + q_lane_bytes(lane);
+    const unsigned char *qlane0 = qb + q_lane_bytes(lane, 0), *qlane1 = qb + q_lane_bytes(lane, 1);
     auto rot = [&](int p) {
         const int pp = p + cr;
         return pp >= np ? pp - np : pp;
@@ -169,15 +170,18 @@ __device__ __forceinline__ void score_pairs(f32x4 (&acc)[KT][HT], const unsigned
 #pragma unroll
                 for (int t = 0; t < PT; ++t) f1[t] = u32x4{0u, 0u, 0u, 0u};
             }
-            // 2*HT query blocks (c, 0..HT-1), (c+1, 0..HT-1) at consecutive KB; reads run two ahead
-            const unsigned char *qc = qlane + ((c * HT) << 10);
+            // query blocks of the pair: chunk c from the even-parity base, c+1 from the odd one,
+            // head tile ht at ht * 2 KB; reads run two ahead
+            const int qoff = (c >> 1) * HT << 11;
+            const unsigned char *qc0 = qlane0 + qoff, *qc1 = qlane1 + qoff;
+            auto qread = [&](int u) { return u < HT ? q_unit(qc0, u) : q_unit(qc1, u - HT); };
             u32x4 bq[2];
-            bq[0] = q_unit(qc, 0);
-            bq[1] = q_unit(qc, 1);
+            bq[0] = qread(0);
+            bq[1] = qread(1);
 #pragma unroll
             for (int u = 0; u < 2 * HT; ++u) {
                 const u32x4 b = bq[u & 1];
-                if (u + 2 < 2 * HT) bq[u & 1] = q_unit(qc, u + 2);
+                if (u + 2 < 2 * HT) bq[u & 1] = qread(u + 2);
 #pragma unroll
                 for (int t = 0; t < PT; ++t)
                     if (l0 + t < MY) acc[l0 + t][u % HT] = mfma_frag<0>(u < HT ? f0[t] : f1[t], b, acc[l0 + t][u % HT]);
@@ -208,8 +212,8 @@ __device__ __forceinline__ void score_dispatch(int my, f32x4 (&acc)[KT][HT], con
 }
 
 // Cooperative staging of a token's queries straight from HBM into LDS; heads >= H read as
-// zero.  bf16: one instruction per 1 KB block (chunk c, head tile ht) of the chunk-major
-// layout, 4 consecutive lanes on each head's 64 bytes.  fp32: each instruction moves up to
+// zero.  bf16: two instructions per 2 KB block (chunk pair, head tile) of the pair-major
+// layout, 8 consecutive lanes on each head's 128 bytes.  fp32: each instruction moves up to
 // 1 KB of one head row.  The loads complete asynchronously (vmcnt); wait before reading.
 template <int DT, int HT, int NW>
 __device__ __forceinline__ void stage_queries(const void *q, int64_t bt, int H, int D, unsigned char *qb, int w,
@@ -218,12 +222,15 @@ __device__ __forceinline__ void stage_queries(const void *q, int64_t bt, int H, 
     const int rowb = D * EB;
     const rsrc_t qr = make_rsrc(reinterpret_cast<const char *>(q) + (size_t)bt * H * D * EB, (uint32_t)(H * D * EB));
     if constexpr (DT == 0) {
-        const int r = lane >> 2;
-        const uint32_t lane_b = 16u * (uint32_t)((lane & 3) ^ qswz(r));
-        const int nch = D >> 5;
-        for (int u = w; u < ((nch + 1) & ~1) * HT; u += NW) {  // odd nch: one zero chunk of padding
-            const int c = u / HT, h = 16 * (u - c * HT) + r;
-            const uint32_t voff = h < H && c < nch ? (uint32_t)(h * rowb + 64 * c) + lane_b : 0x80000000u;
+        // two instructions per 2 KB block, 8 heads x 128 bytes each (8 lanes to a row)
+        const int nch = D >> 5, npair = (nch + 1) >> 1;
+        const int rin = lane >> 3;
+        for (int u = w; u < npair * HT * 2; u += NW) {
+            const int blk = u >> 1, half = u & 1;
+            const int p = blk / HT, r = 8 * half + rin, h = 16 * (blk - p * HT) + r;
+            const int x = (lane & 7) ^ ((r >> 1) & 7);  // segment landing at slot lane&7
+            const bool ok = h < H && 2 * p + (x >> 2) < nch;  // odd nch: the pair's 2nd chunk is zero
+            const uint32_t voff = ok ? (uint32_t)(h * rowb + 128 * p + 16 * x) : 0x80000000u;
             buf_load_lds16(qr, qb + (u << 10), voff);
         }
     } else {
@@ -619,7 +626,7 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
 template <int DT, int HT, int KT, int NW, bool FUSED>
 hipError_t launch3(const TargetArgs &a, hipStream_t stream) {
     const size_t red = (size_t)NW * 16 * HT * 4;
-    const size_t qbytes = DT == 0 ? (size_t)1024 * HT * (((a.D >> 5) + 1) & ~1) : (size_t)16 * HT * (a.D * 4 + 16);
+    const size_t qbytes = DT == 0 ? (size_t)2048 * HT * (((a.D >> 5) + 1) >> 1) : (size_t)16 * HT * (a.D * 4 + 16);
     const size_t lds = qbytes + (size_t)8 * a.K + 2 * red + (size_t)NW * 4 +
                        (size_t)2 * NW * 4 + (FUSED ? 2 * red : 0);
     if (lds > 160 * 1024) return hipErrorInvalidValue;

@@ -292,14 +292,25 @@ __device__ __forceinline__ int compact_slots(const int32_t *idr, int K, int N, f
 // (g, x) = (lane/16, lane%16) holds rows 4g+i of each tile for heads 16ht+x.
 
 // Per-head maximum and sum of exp2 over this wave's slots (log2 domain, scale > 0),
-// published in red_m/red_s laid out [wave][head%16][head tile].  Padding rows of a
-// partial last tile were scored against a valid selected row (crow[0]), so they repeat
-// a real score and leave the maximum exact; only their exponentials are zeroed.  On
-// return acc holds exp2(c - mloc).
+// published in red_m/red_s laid out [wave][head%16][head tile].  Padding rows of the
+// partial last tile (at most one per wave) are set to -inf first, so every later step
+// sees only real slots.  On return acc holds exp2(c - mloc).
 template <int HT, int KT, int NW>
 __device__ __forceinline__ void epi_stats(f32x4 (&acc)[KT][HT], float (&mloc)[HT], int my, int nv, int w, int lane,
                                           float scale_log2, float *red_m, float *red_s) {
     const int x = lane & 15, prow = 4 * (lane >> 4);
+#pragma unroll
+    for (int l = 0; l < KT; ++l) {
+        const int base = 16 * (w + l * NW);
+        if (l < my && base + 16 > nv) {  // uniform: the partial tile
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool pad = base + prow + i >= nv;
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht) acc[l][ht][i] = pad ? -INFINITY : acc[l][ht][i];
+            }
+        }
+    }
     float sloc[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
@@ -321,26 +332,8 @@ __device__ __forceinline__ void epi_stats(f32x4 (&acc)[KT][HT], float (&mloc)[HT
                 acc[l][ht][i] = e;
                 sum += e;
             }
-        sloc[ht] = sum;
+        sloc[ht] = cols4_sum(sum);
     }
-#pragma unroll
-    for (int l = 0; l < KT; ++l) {
-        const int base = 16 * (w + l * NW);
-        if (l < my && base + 16 > nv) {  // the partial tile (at most one per wave)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (base + prow + i >= nv) {
-#pragma unroll
-                    for (int ht = 0; ht < HT; ++ht) {
-                        sloc[ht] -= acc[l][ht][i];
-                        acc[l][ht][i] = 0.f;
-                    }
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) sloc[ht] = cols4_sum(sloc[ht]);
     if (lane < 16) {
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
@@ -350,19 +343,37 @@ __device__ __forceinline__ void epi_stats(f32x4 (&acc)[KT][HT], float (&mloc)[HT
     }
 }
 
-// After the barrier that publishes red_m/red_s: the joint denominator per head,
-// full_h = log2(sum_k 2^c_hk + 2^(nc_lse_h log2 e)); lane (g, x) reduces head 16g+x over
-// the waves and every lane fetches the HT heads it holds.  This wave's exp2(c - mloc)
-// values carry weight 2^(mloc - full); their head sums m_k (16-lane row reduction) are
-// returned in m and the wave's row mass goes to red_t[w].  nc: the natural-log nc_lse of
-// head 16*min(g, HT-1)+x (ignored when has_nc is false).
+// One butterfly step of a 16-lane transpose-reduction: lanes whose bit `bit` is clear keep
+// the first half of their n values, the others the second half, each adding what its
+// partner (the lane the DPP control reads from, which differs in that bit) sends.
+template <int CTRL, int N>
+__device__ __forceinline__ void tr_step(float (&v)[16], bool hi) {
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k) {
+        const float a = v[k], b = v[k + N / 2];
+        const float keep = hi ? b : a, send = hi ? a : b;
+        v[k] = keep + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), CTRL,
+                                                                            0xf, 0xf, false));
+    }
+}
+
+// After the barrier that publishes red_m/red_s: the target row of this wave's slots.
+//   full_h = log2(sum_k 2^c_hk + 2^(nc_h log2 e))  (lane (g, x) reduces head 16g+x over waves)
+//   row total sum_k m_k = sum_h 2^(clse_h - full_h), clse_h = log2 sum_k 2^c_hk, which needs
+//   no further exchange between waves
+//   T_k = sum_h exp2(c_hk - mloc_h) * 2^(mloc_h - full_h) / max(total, floor)
+// The head sum is a 16-lane transpose-reduction: afterwards lane (g, x) holds T of row
+// 4g + (x%4) of tile x/4 and stores it at its slot.  nc: the natural-log nc_lse of head
+// 16*min(g, HT-1)+x (ignored when has_nc is false).
 template <int HT, int KT, int NW>
-__device__ __forceinline__ void epi_rows(const f32x4 (&acc)[KT][HT], const float (&mloc)[HT], float (&m)[KT][4], int my,
-                                         int w, int lane, int H, bool has_nc, float nc, const float *red_m,
-                                         const float *red_s, float *red_t) {
+__device__ __forceinline__ void epi_target(const f32x4 (&acc)[KT][HT], const float (&mloc)[HT], int my, int nv, int w,
+                                           int lane, int H, bool has_nc, float nc, float l1_floor, const float *red_m,
+                                           const float *red_s, const int32_t *cslot, float *Tr) {
+    static_assert(KT <= 4, "at most 16 rows per lane");
     const int x = lane & 15, g = lane >> 4;
     const int gg = g < HT ? g : HT - 1;
-    float fullv;
+    const bool head_ok = g < HT && gg * 16 + x < H;
+    float full, share;
     {
         float M = -INFINITY;
 #pragma unroll 4
@@ -371,53 +382,36 @@ __device__ __forceinline__ void epi_rows(const f32x4 (&acc)[KT][HT], const float
 #pragma unroll 4
         for (int i = 0; i < NW; ++i)
             ssum = fmaf(red_s[(i * 16 + x) * HT + gg], fast_exp2(red_m[(i * 16 + x) * HT + gg] - M), ssum);
-        fullv = M + fast_log2(ssum);
-        if (has_nc && gg * 16 + x < H) fullv = logaddexp2(fullv, nc * kLog2e);
+        const float clse = M + fast_log2(ssum);
+        full = (has_nc && head_ok) ? logaddexp2(clse, nc * kLog2e) : clse;
+        share = head_ok ? fast_exp2(clse - full) : 0.f;  // this head's share of the joint mass
     }
+    const float tot = cols4_sum(row16_sum(share));
+    const float rden = 1.f / fmaxf(tot, l1_floor);
     float wgt[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-        const float full = __shfl(fullv, ht * 16 + x);
-        wgt[ht] = (ht * 16 + x < H && mloc[ht] != -INFINITY) ? fast_exp2(mloc[ht] - full) : 0.f;
+        const float f = __shfl(full, ht * 16 + x);
+        wgt[ht] = (ht * 16 + x < H && mloc[ht] != -INFINITY) ? fast_exp2(mloc[ht] - f) * rden : 0.f;
     }
-    float part = 0.f;
+    float v[16];
 #pragma unroll
-    for (int l = 0; l < KT; ++l)
+    for (int l = 0; l < 4; ++l)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float sum = 0.f;
-            if (l < my) {
+            if (l < KT) {
 #pragma unroll
                 for (int ht = 0; ht < HT; ++ht) sum = fmaf(acc[l][ht][i], wgt[ht], sum);
-                sum = row16_sum(sum);
             }
-            m[l][i] = sum;
-            part += sum;  // padding rows hold exactly 0
+            v[4 * l + i] = sum;
         }
-    part = cols4_sum(part);
-    if (lane == 0) red_t[w] = part;
-}
-
-// After the barrier that publishes red_t: L1 normalisation and the scatter back to slot
-// order (lane (g, x < 4) stores row 4g + x of each tile).
-template <int KT, int NW>
-__device__ __forceinline__ void epi_scatter(const float (&m)[KT][4], int my, int nv, int w, int lane,
-                                            const float *red_t, float l1_floor, const int32_t *cslot, float *Tr) {
-    const int x = lane & 15, prow = 4 * (lane >> 4);
-    float tot = 0.f;
-#pragma unroll 4
-    for (int i = 0; i < NW; ++i) tot += red_t[i];
-    const float rden = 1.f / fmaxf(tot, l1_floor);
-    if (x < 4) {
-#pragma unroll
-        for (int l = 0; l < KT; ++l) {
-            const int pos = 16 * (w + l * NW) + prow + x;
-            if (l < my && pos < nv) {
-                const float val = x == 0 ? m[l][0] : x == 1 ? m[l][1] : x == 2 ? m[l][2] : m[l][3];
-                Tr[cslot[pos]] = val * rden;
-            }
-        }
-    }
+    tr_step<0x128, 16>(v, (x & 8) != 0);  // row_ror:8      partner x^8
+    tr_step<0x141, 8>(v, (x & 4) != 0);   // row_half_mirror partner x^7
+    tr_step<0x4e, 4>(v, (x & 2) != 0);    // quad_perm 2301 partner x^2
+    tr_step<0xb1, 2>(v, (x & 1) != 0);    // quad_perm 1032 partner x^1
+    const int l = x >> 2, pos = 16 * (w + l * NW) + 4 * g + (x & 3);
+    if (l < KT && l < my && pos < nv) Tr[cslot[pos]] = v[0];
 }
 
 // Arguments of the target kernels (one struct in the kernel-argument segment).
@@ -536,8 +530,7 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
     int32_t *cslot = crow + K;                                                // [K] slot index per compacted slot
     float *red_m = reinterpret_cast<float *>(cslot + K);                      // [NW][16][HT] per-wave head max
     float *red_s = red_m + NW * 16 * HT;                                      // [NW][16][HT] per-wave head sum
-    float *red_t = red_s + NW * 16 * HT;                                      // [NW] per-wave row mass
-    int *wcnt = reinterpret_cast<int *>(red_t + NW);                          // [KP][NW] valid-slot counts
+    int *wcnt = reinterpret_cast<int *>(red_s + NW * 16 * HT);                // [KP][NW] valid-slot counts
     float *red_wm = reinterpret_cast<float *>(wcnt + KP * NW);                // FUSED: [NW][16][HT] window max
     float *red_ws = red_wm + NW * 16 * HT;                                    // FUSED: [NW][16][HT] window sum
 
@@ -615,20 +608,18 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
         asm volatile("" : "+v"(t));
         lane = t & 63;
     }
-    float mloc[HT], m[KT][4];
+    float mloc[HT];
     epi_stats<HT, KT, NW>(acc, mloc, my, nv, w, lane, a.scale_log2, red_m, red_s);
     __syncthreads();
-    epi_rows<HT, KT, NW>(acc, mloc, m, my, w, lane, H, FUSED || a.nc_lse != nullptr, nc, red_m, red_s, red_t);
-    __syncthreads();
-    epi_scatter<KT, NW>(m, my, nv, w, lane, red_t, a.l1_floor, cslot, Tr);
+    epi_target<HT, KT, NW>(acc, mloc, my, nv, w, lane, H, FUSED || a.nc_lse != nullptr, nc, a.l1_floor, red_m, red_s,
+                           cslot, Tr);
 }
 
 template <int DT, int HT, int KT, int NW, bool FUSED>
 hipError_t launch3(const TargetArgs &a, hipStream_t stream) {
     const size_t red = (size_t)NW * 16 * HT * 4;
     const size_t qbytes = DT == 0 ? (size_t)2048 * HT * (((a.D >> 5) + 1) >> 1) : (size_t)16 * HT * (a.D * 4 + 16);
-    const size_t lds = qbytes + (size_t)8 * a.K + 2 * red + (size_t)NW * 4 +
-                       (size_t)2 * NW * 4 + (FUSED ? 2 * red : 0);
+    const size_t lds = qbytes + (size_t)8 * a.K + 2 * red + (size_t)2 * NW * 4 + (FUSED ? 2 * red : 0);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     auto kfn = &distill_target_kernel<DT, HT, KT, NW, FUSED>;
     if (lds > 65536) {  // opt in to more than 64 KiB of LDS per workgroup (gfx950 has 160 KiB per CU)

@@ -148,9 +148,9 @@ int distill_target_fused(const void *q, const void *kwin, const float *sink, con
  *   target, logits [B,S,K] float32;  idx [B,S,K] int32 (validity only, 0 <= idx < N)
  *   kl_rows [B,S] float32 out;  dlogits [B,S,K] float32 out or NULL (forward only)
  *   stats [2] float32 out
- *   workspace: device scratch of distill_kl_workspace_bytes(B,S,K) bytes, owned by the
- *   caller; its contents need no initialisation and are overwritten.  Calls that share
- *   a workspace must be ordered (same stream).
+ *   workspace: device scratch of distill_kl_workspace_bytes(B,S,K) bytes, 16-byte
+ *   aligned, owned by the caller; its contents need no initialisation and are
+ *   overwritten.  Calls that share a workspace must be ordered (same stream).
  * Limits: K <= 4096.
  */
 size_t distill_kl_workspace_bytes(int B, int S, int K);

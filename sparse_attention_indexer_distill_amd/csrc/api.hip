@@ -2,6 +2,7 @@
 // kernel launches on the caller's stream.  Validation happens entirely on the host and
 // before any HIP call, so every rejection path is exercised without a GPU.
 #include <math.h>
+#include <stdint.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -123,6 +124,8 @@ int distill_kl_fwd_bwd(const float *target, const float *logits, const int32_t *
     const size_t need = sd::kl_workspace_bytes(B, S, K);
     if (workspace_bytes < need)
         return fail(SD_ERR_BAD_SHAPE, "distill_kl_fwd_bwd: workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if ((uintptr_t)workspace % 16 != 0)
+        return fail(SD_ERR_BAD_SHAPE, "distill_kl_fwd_bwd: workspace must be 16-byte aligned");
     return hip_status(sd::launch_distill_kl(target, logits, idx, B, S, K, N, grad_scale, kl_rows, dlogits, stats,
                                             workspace, stream),
                       "distill_kl_fwd_bwd launch");

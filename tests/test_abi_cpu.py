@@ -138,6 +138,7 @@ def test_distill_kl_rejections(lib):
     assert _kl(lib, wsb=7) == sd.SD_ERR_BAD_SHAPE  # one 8-row block needs 8 bytes
     assert b"workspace" in lib.sd_last_error()
     assert _kl(lib, K=4097) == sd.SD_ERR_UNSUPPORTED
+    assert _kl(lib, ws=ctypes.c_void_p(0x1004)) == sd.SD_ERR_BAD_SHAPE   # not 16-byte aligned
 
 
 def test_binding_rejects_host_tensors():

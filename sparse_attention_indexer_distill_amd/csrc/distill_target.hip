@@ -434,11 +434,12 @@ struct TargetArgs {
 // the LSE over {scale <q_h, kwin_j> : j in [max(0, t-W+1), t], seg[j] == seg[t]} plus the
 // sink, per head.  Window tiles of 16 consecutive keys starting at the first key are dealt
 // to the waves like slot tiles (at most KWT per wave) and scored with the same MFMA loop
-// against the staged queries; masked per-wave statistics are combined through red_wm/red_ws
-// (one barrier).  Returns, in natural log, the value of head 16*min(g, HT-1) + x for lane
-// (g, x) -- the layout the epilogue takes its nc values in.
+// against the staged queries.  window_local publishes each wave's masked per-head maximum
+// and sum in red_wm/red_ws without waiting; after the epilogue's barrier window_combine
+// reduces them over the waves and adds the sink, returning in natural log the value of head
+// 16*min(g, HT-1) + x for lane (g, x) -- the layout the epilogue takes its nc values in.
 template <int DT, int HT, int NW, int KWT>
-__device__ __forceinline__ float window_part(const TargetArgs &a, const unsigned char *qb, int RS, int b, int t, int w,
+__device__ __forceinline__ void window_local(const TargetArgs &a, const unsigned char *qb, int RS, int b, int t, int w,
                                              int lane, float *red_wm, float *red_ws) {
     constexpr int EB = Elem<DT>::bytes;
     const int S = a.S, D = a.D, nch = D >> 5;
@@ -496,7 +497,12 @@ __device__ __forceinline__ float window_part(const TargetArgs &a, const unsigned
             red_ws[(w * 16 + x) * HT + ht] = sum;
         }
     }
-    __syncthreads();
+}
+
+template <int HT, int NW>
+__device__ __forceinline__ float window_combine(const TargetArgs &a, int lane, const float *red_wm,
+                                                const float *red_ws) {
+    const int x = lane & 15, g = lane >> 4;
     const int gg = g < HT ? g : HT - 1;
     float M = -INFINITY;
 #pragma unroll 4
@@ -514,7 +520,7 @@ __device__ __forceinline__ float window_part(const TargetArgs &a, const unsigned
 }
 
 // One workgroup per token (latest tokens first, they hold the most valid slots).  FUSED:
-// the window part of the joint softmax is computed here too (window_part) instead of being
+// the window part of the joint softmax is computed here too (window_local) instead of being
 // read from nc_lse, so the queries are read from HBM once for the whole target.
 template <int DT, int HT, int KT, int NW, bool FUSED>
 __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kernel(const TargetArgs a) {
@@ -546,17 +552,27 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
     __builtin_amdgcn_s_waitcnt(0);  // this wave's query loads have landed in LDS
     __syncthreads();                // ... and everyone else's; the compacted list is complete
 
-    // nc value (natural log) of head 16*min(g, HT-1) + x for lane (g, x)
+    // nc value (natural log) of head 16*min(g, HT-1) + x for lane (g, x).  FUSED: the
+    // window statistics are published now and combined after the epilogue's barrier.
     float nc = 0.f;
-    if constexpr (FUSED) {
-        nc = window_part<DT, HT, NW, KWT>(a, qb, RS, b, (int)(bt - (int64_t)b * S), w, lane, red_wm, red_ws);
+    auto window_done = [&]() {
+        nc = window_combine<HT, NW>(a, lane, red_wm, red_ws);
         const int g = lane >> 4, h = 16 * g + (lane & 15);
         if (a.nc_out != nullptr && g < HT && h < H) a.nc_out[bt * H + h] = nc;
+    };
+    if constexpr (FUSED) {
+        window_local<DT, HT, NW, KWT>(a, qb, RS, b, (int)(bt - (int64_t)b * S), w, lane, red_wm, red_ws);
     } else {
         const int h = 16 * ((lane >> 4) < HT ? (lane >> 4) : HT - 1) + (lane & 15);
         if (a.nc_lse != nullptr && h < H) nc = a.nc_lse[bt * H + h];
     }
-    if (nv == 0) return;            // empty row: already all zeros
+    if (nv == 0) {                  // empty row: the target is already all zeros
+        if constexpr (FUSED) {
+            __syncthreads();
+            window_done();
+        }
+        return;
+    }
 
     // 2. Scores of this wave's slot tiles: tiles w, w+NW, w+2NW, ... of the compacted list.
     const int ntiles = (nv + 15) >> 4;
@@ -611,6 +627,7 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
     float mloc[HT];
     epi_stats<HT, KT, NW>(acc, mloc, my, nv, w, lane, a.scale_log2, red_m, red_s);
     __syncthreads();
+    if constexpr (FUSED) window_done();
     epi_target<HT, KT, NW>(acc, mloc, my, nv, w, lane, H, FUSED || a.nc_lse != nullptr, nc, a.l1_floor, red_m, red_s,
                            cslot, Tr);
 }

@@ -1,9 +1,12 @@
 """Benchmark: ms per CSA layer of the indexer-distillation hot path on one MI355X.
 
-One step = window_lse -> distill_target -> distill_kl_fwd_bwd (forward and backward to the
-student logits) over one V4-Flash-shaped CSA layer (B=1, S=4096, H=64, D=512, pool N=1024,
-top-k K=512, window W=128; bf16 q / pool / window keys, fp32 sink and student logits,
-uniform causal top-k slots), with every input resident in HBM before the timed region.
+One step is the whole path over one V4-Flash-shaped CSA layer (B=1, S=4096, H=64, D=512,
+pool N=1024, top-k K=512, window W=128; bf16 q / pool / window keys, fp32 sink and student
+logits, uniform causal top-k slots), with every input resident in HBM before the timed
+region: the window-LSE, the joint target, and the KL forward with its backward to the
+student logits.  The default path runs distill_target_fused (window part and target in one
+pass, nc_lse written as a by-product) -> distill_kl_fwd_bwd; --path 3call runs
+window_lse -> distill_target -> distill_kl_fwd_bwd.  Both compute the same outputs.
 
 Prints ONE JSON line.  `value` is the wall-clock ms per layer over the timed steps
 (bracketed by device synchronisation).  Per-kernel durations come from HIP events recorded
@@ -152,7 +155,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="c3", choices=["c3", "c4", "c5"])
-    ap.add_argument("--path", default="3call", choices=["3call", "fused"],
+    ap.add_argument("--path", default="fused", choices=["3call", "fused"],
                     help="3call: window_lse -> distill_target -> KL; fused: distill_target_fused -> KL")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",

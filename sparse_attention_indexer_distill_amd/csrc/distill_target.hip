@@ -388,12 +388,12 @@ __device__ __forceinline__ void epi_target(const f32x4 (&acc)[KT][HT], const flo
     }
     const float tot = cols4_sum(row16_sum(share));
     const float rden = 1.f / fmaxf(tot, l1_floor);
+    float fr[4];
+    rows_bcast(full, fr);  // fr[ht]: full of head 16ht + x
     float wgt[HT];
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        const float f = __shfl(full, ht * 16 + x);
-        wgt[ht] = (ht * 16 + x < H && mloc[ht] != -INFINITY) ? fast_exp2(mloc[ht] - f) * rden : 0.f;
-    }
+    for (int ht = 0; ht < HT; ++ht)
+        wgt[ht] = (ht * 16 + x < H && mloc[ht] != -INFINITY) ? fast_exp2(mloc[ht] - fr[ht]) * rden : 0.f;
     float v[16];
 #pragma unroll
     for (int l = 0; l < 4; ++l)

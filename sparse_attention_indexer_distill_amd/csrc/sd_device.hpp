@@ -188,28 +188,66 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
+// Cross-row exchanges on the VALU (gfx950 v_permlane16_swap / v_permlane32_swap, no LDS
+// traffic).  With both operands equal to v, the pair returned in lane l is
+// {v[l & ~16], v[l | 16]} (16-lane swap) or {v[l & 31], v[l | 32]} (32-lane swap): the lane's
+// own value and its partner's at xor 16 or xor 32, in the same order in both partners, so
+// both get bitwise equal results.
+__device__ __forceinline__ void xrow16(float v, float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v),
+                                                    false, false);
+    a = __builtin_bit_cast(float, (uint32_t)r[0]);
+    b = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ __forceinline__ void xrow32(float v, float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v),
+                                                    false, false);
+    a = __builtin_bit_cast(float, (uint32_t)r[0]);
+    b = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
 // Combine the four DPP rows holding the same column (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float cols4_max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    float a, b;
+    xrow16(v, a, b);
+    xrow32(fmaxf(a, b), a, b);
+    return fmaxf(a, b);
 }
 __device__ __forceinline__ float cols4_sum(float v) {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
+    float a, b;
+    xrow16(v, a, b);
+    xrow32(a + b, a, b);
+    return a + b;
+}
+
+// Value of DPP row R (lanes 16R + l%16) of v in every lane, for R = 0..3.
+__device__ __forceinline__ void rows_bcast(float v, float (&out)[4]) {
+    float e, o;
+    xrow16(v, e, o);           // rows 0/2 and rows 1/3 of v, by half
+    xrow32(e, out[0], out[2]);
+    xrow32(o, out[1], out[3]);
+}
+
+// Butterfly over the 16 lanes of a DPP row with partners x^8, x^7, x^2, x^1 (row_ror:8,
+// row_half_mirror, quad_perm [2,3,0,1], quad_perm [1,0,3,2]); the pairings generate the
+// whole row, and each pair adds or compares the same two values, so every lane of the row
+// ends with the same result.
+template <bool MAX>
+__device__ __forceinline__ float row16_butterfly(float v) {
+    float p;
+    p = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+    v = MAX ? fmaxf(v, p) : v + p;
+    p = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xf, 0xf, false));
+    v = MAX ? fmaxf(v, p) : v + p;
+    p = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4e, 0xf, 0xf, false));
+    v = MAX ? fmaxf(v, p) : v + p;
+    p = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xb1, 0xf, 0xf, false));
+    v = MAX ? fmaxf(v, p) : v + p;
     return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return cols4_max(row16_butterfly<true>(v)); }
+__device__ __forceinline__ float wave_sum(float v) { return cols4_sum(row16_butterfly<false>(v)); }
 
 // exp2 / log2 on the hardware transcendental unit.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

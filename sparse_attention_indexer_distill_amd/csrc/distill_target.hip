@@ -10,17 +10,17 @@
 // the pool is indexed inside the kernel, so no [B,S,K,D] gather is materialised).
 //
 // Mapping.  One workgroup per token, NW waves.  The token's queries (all heads) are
-// staged once in LDS in MFMA fragment order.  The valid slots of the row are compacted
-// (stable, slot order) into a list in LDS; 16-slot tiles of that list are dealt
-// round-robin to the waves, so invalid (-1) slots cost no MFMA work wherever they sit.
-// Each wave streams its rows' fragments straight from L2 with buffer loads (each lane
-// reads 16 contiguous bytes of one pool row per 32-wide D chunk, one chunk ahead of the
-// MFMAs) and accumulates
+// staged once in LDS.  The valid slots of the row are compacted (stable, slot order) into
+// a list in LDS; 16-slot tiles of that list are dealt round-robin to the waves, so invalid
+// (-1) slots cost no MFMA work wherever they sit.  Each wave gathers its rows from L2 in
+// 128-byte pieces (8 consecutive lanes on a row, the layout the memory pipeline merges),
+// regroups them into MFMA operand fragments with one ds_bpermute per dword, and
+// accumulates
 //     C[slot][head] (16x16 tiles) = pool_row . q_head
-// for all heads, keeping every score of its slots in registers.  The per-head maximum
-// and sum (log2 domain) need two cross-lane steps plus one LDS exchange between waves;
-// the head sum of p[h,k] = exp(c[h,k] - full_h) is a 16-lane DPP reduction.  Nothing but
-// the target row is written.
+// for all heads, keeping every score of its slots in registers.  The epilogue has one
+// barrier: per-wave head statistics cross waves through LDS, the row's joint mass follows
+// from them without a second exchange, and the head sum of p[h,k] = exp(c[h,k] - full_h)
+// is a 16-lane DPP transpose-reduction.  Nothing but the target row is written.
 #include <float.h>
 
 #include "sd_device.hpp"

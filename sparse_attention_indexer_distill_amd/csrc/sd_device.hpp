@@ -74,10 +74,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t byte_off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
-}
-
 // Device-scope (sc1) load: served by L2 without allocating in the CU's L1.  Used for row
 // gathers, which have no L1 reuse and whose 1 KB-strided rows otherwise pile into a few L1
 // sets (tag-conflict stalls).
@@ -103,20 +99,6 @@ __device__ __forceinline__ f32x8 buf_load_frag<1>(rsrc_t r, uint32_t byte_off) {
 // `lds` must be wave-uniform.  Completion is tracked by vmcnt (wait before reading).
 __device__ __forceinline__ void buf_load_lds16(rsrc_t r, void *lds, uint32_t byte_off) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, byte_off, 0, 0, 0);
-}
-
-// A fragment stored in LDS as NH = sizeof(frag)/16 planes of 64 lanes x 16 bytes.
-template <int DT>
-__device__ __forceinline__ typename Elem<DT>::frag_t lds_frag(const u32x4 *units, int unit);
-template <>
-__device__ __forceinline__ u32x4 lds_frag<0>(const u32x4 *units, int unit) {
-    return units[unit];
-}
-template <>
-__device__ __forceinline__ f32x8 lds_frag<1>(const u32x4 *units, int unit) {
-    const f32x4 lo = __builtin_bit_cast(f32x4, units[unit]);
-    const f32x4 hi = __builtin_bit_cast(f32x4, units[unit + 64]);
-    return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 // ---- coalesced row gathers ---------------------------------------------------------

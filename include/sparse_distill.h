@@ -68,7 +68,8 @@ enum { SD_BF16 = 0, SD_F32 = 1 };
  *   sink   [H]        float32 or NULL per-head sink logit; NULL drops the term
  *   seg    [B,S]      int32 or NULL   packed-segment ids; NULL = one segment
  *   nc_lse [B,S,H]    float32 out     natural-log mass (never -inf: j = t is in win(t))
- * Limits: D % 32 == 0, D <= 512; H <= 64; 1 <= W <= 128.
+ * Limits: D % 32 == 0, D <= 512; H <= 64; 1 <= W <= 128; S * D * element size < 2^31
+ * bytes (one batch row of kwin).
  */
 int window_lse(const void *q, const void *kwin, const float *sink, const int32_t *seg,
                int B, int S, int H, int D, int W, float scale, int dtype, float *nc_lse,
@@ -98,8 +99,9 @@ int window_lse(const void *q, const void *kwin, const float *sink, const int32_t
  *   scale            softmax scale, positive and finite (1/sqrt(D) for the method)
  *   l1_floor         <= 0 selects FLT_MIN (2^-126); 1e-10 reproduces the legacy floor
  *   target [B,S,K]   float32 out      a row with no valid slot is all zeros
- * Limits: D % 32 == 0, D <= 512; H <= 64; K <= 1024.  A non-positive or non-finite
- * scale is rejected with SD_ERR_BAD_SHAPE.
+ * Limits: D % 32 == 0, D <= 512; H <= 64; K <= 1024; N * D * element size < 2^31 bytes
+ * (one batch row of pool).  A non-positive or non-finite scale is rejected with
+ * SD_ERR_BAD_SHAPE.
  */
 int distill_target(const void *q, const void *pool, const int32_t *idx, const float *nc_lse,
                    int B, int S, int H, int D, int N, int K, float scale, float l1_floor,

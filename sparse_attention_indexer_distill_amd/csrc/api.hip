@@ -42,6 +42,17 @@ int check_common(int dtype, int B, int S, int H, int D) {
     return SD_OK;
 }
 
+// The kernels address one batch row of pool or window keys through a 32-bit buffer range
+// with 32-bit signed row offsets (row * D * element size), so each such row must stay
+// below 2^31 bytes.
+int check_rows(const char *fn, const char *what, int64_t rows, int D, int dtype) {
+    const int64_t eb = dtype == SD_F32 ? 4 : 2;
+    if (rows * D * eb > (((int64_t)1 << 31) - 1))
+        return fail(SD_ERR_UNSUPPORTED, "%s: %s of %lld rows x D=%d exceeds 2^31 bytes per batch", fn, what,
+                    (long long)rows, D);
+    return SD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -68,6 +79,7 @@ int window_lse(const void *q, const void *kwin, const float *sink, const int32_t
     if (W <= 0) return fail(SD_ERR_BAD_SHAPE, "window_lse: W=%d must be positive", W);
     if (W > sd::kMaxWindow) return fail(SD_ERR_UNSUPPORTED, "window_lse: W=%d exceeds %d", W, sd::kMaxWindow);
     if (!isfinite(scale)) return fail(SD_ERR_BAD_SHAPE, "window_lse: scale must be finite");
+    if ((st = check_rows("window_lse", "kwin", S, D, dtype)) != SD_OK) return st;
     return hip_status(sd::launch_window_lse(q, kwin, sink, seg, B, S, H, D, W, scale, dtype, nc_lse, stream),
                       "window_lse launch");
 }
@@ -82,6 +94,7 @@ int distill_target(const void *q, const void *pool, const int32_t *idx, const fl
     if (K > sd::kMaxTopK) return fail(SD_ERR_UNSUPPORTED, "distill_target: K=%d exceeds %d", K, sd::kMaxTopK);
     if (!isfinite(scale) || !(scale > 0.f) || isnan(l1_floor))
         return fail(SD_ERR_BAD_SHAPE, "distill_target: scale must be positive and finite, l1_floor not NaN");
+    if ((st = check_rows("distill_target", "pool", N, D, dtype)) != SD_OK) return st;
     return hip_status(sd::launch_distill_target(q, pool, idx, nc_lse, B, S, H, D, N, K, scale, l1_floor, dtype,
                                                 target, stream),
                       "distill_target launch");
@@ -100,6 +113,8 @@ int distill_target_fused(const void *q, const void *kwin, const float *sink, con
     if (W > sd::kMaxWindow) return fail(SD_ERR_UNSUPPORTED, "distill_target_fused: W=%d exceeds %d", W, sd::kMaxWindow);
     if (!isfinite(scale) || !(scale > 0.f) || isnan(l1_floor))
         return fail(SD_ERR_BAD_SHAPE, "distill_target_fused: scale must be positive and finite, l1_floor not NaN");
+    if ((st = check_rows("distill_target_fused", "pool", N, D, dtype)) != SD_OK) return st;
+    if ((st = check_rows("distill_target_fused", "kwin", S, D, dtype)) != SD_OK) return st;
     return hip_status(sd::launch_distill_target_fused(q, kwin, sink, seg, pool, idx, B, S, H, D, N, K, W, scale,
                                                       l1_floor, dtype, target, nc_lse_out, stream),
                       "distill_target_fused launch");

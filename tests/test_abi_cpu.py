@@ -71,6 +71,10 @@ def test_window_lse_rejections(lib):
     assert _wl(lib, H=65) == sd.SD_ERR_UNSUPPORTED
     assert _wl(lib, W=129) == sd.SD_ERR_UNSUPPORTED
     assert b"W=129" in lib.sd_last_error()
+    # one batch row of window keys must stay below 2^31 bytes (32-bit buffer offsets)
+    assert _wl(lib, S=1 << 21, D=512) == sd.SD_ERR_UNSUPPORTED            # exactly 2^31 bytes of bf16
+    assert b"2^31" in lib.sd_last_error()
+    assert _wl(lib, S=1 << 20, D=512, dtype=1) == sd.SD_ERR_UNSUPPORTED   # fp32
 
 
 def _tg(lib, q=FAKE, pool=FAKE, idx=FAKE, out=FAKE, B=1, S=8, H=4, D=32, N=2, K=4, scale=0.1, floor=0.0, dtype=0):
@@ -92,6 +96,8 @@ def test_distill_target_rejections(lib):
     assert _tg(lib, K=1025) == sd.SD_ERR_UNSUPPORTED
     assert _tg(lib, D=16) == sd.SD_ERR_UNSUPPORTED
     assert _tg(lib, H=128) == sd.SD_ERR_UNSUPPORTED
+    assert _tg(lib, N=1 << 21, D=512) == sd.SD_ERR_UNSUPPORTED           # pool row of 2^31 bytes
+    assert b"pool" in lib.sd_last_error()
 
 
 def _tf(lib, q=FAKE, k=FAKE, pool=FAKE, idx=FAKE, out=FAKE, B=1, S=8, H=4, D=32, N=2, K=4, W=4, scale=0.1,
@@ -117,6 +123,10 @@ def test_distill_target_fused_rejections(lib):
     assert _tf(lib, K=1025) == sd.SD_ERR_UNSUPPORTED
     assert _tf(lib, D=48) == sd.SD_ERR_UNSUPPORTED
     assert b"head dim" in lib.sd_last_error()
+    assert _tf(lib, N=1 << 21, D=512) == sd.SD_ERR_UNSUPPORTED
+    assert b"pool" in lib.sd_last_error()
+    assert _tf(lib, S=1 << 21, D=512) == sd.SD_ERR_UNSUPPORTED
+    assert b"kwin" in lib.sd_last_error()
 
 
 def _kl(lib, T=FAKE, z=FAKE, idx=FAKE, B=1, S=8, K=4, N=2, g=1.0, rows=FAKE, dz=FAKE, st=FAKE, ws=FAKE,

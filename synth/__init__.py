@@ -181,13 +181,21 @@ def sample_rows(cfg: Config | str, n: int, seed_offset: int = 0) -> np.ndarray:
     """Seeded sorted sample of flat row ids (b*S+t) for sampled parity checks.
 
     Always includes the first and last rows of every batch so the empty-row head of
-    the sequence and its fullest tail are both covered."""
+    the sequence and its fullest tail are both covered, the rows around t = 4K where a
+    row's visible blocks first outnumber its K slots (all blocks, padded with -1, give
+    way to a random K of them), and the rows around every segment start."""
     if isinstance(cfg, str):
         cfg = CONFIGS[cfg]
     total = cfg.B * cfg.S
     rng = np.random.Generator(np.random.PCG64(1000 * cfg.cid + TENSOR_ID["rowpick"] + 100 + seed_offset))
     pick = rng.choice(total, size=min(n, total), replace=False)
     edges = []
+    L = cfg.S // max(cfg.segments, 1)
     for b in range(cfg.B):
         edges += [b * cfg.S, b * cfg.S + 1, b * cfg.S + 3, b * cfg.S + 4, (b + 1) * cfg.S - 1]
+        for s0 in range(0, cfg.S, L):                       # segment starts
+            sat = s0 + COMPRESS_RATIO * cfg.K               # n_v = floor((t_loc+1)/4) first exceeds K
+            for t in (s0 - 1, s0, s0 + 3, s0 + 4, sat - 2, sat - 1, sat, sat + 1):
+                if 0 <= t < cfg.S:
+                    edges.append(b * cfg.S + t)
     return np.unique(np.concatenate([pick, np.array(edges)])).astype(np.int64)

@@ -148,21 +148,23 @@ __global__ __launch_bounds__(kWinTok * 64) void window_lse_kernel(
 }
 
 // ---------------------------------------------------------------------------------
-// bf16 fast path (D % 64 == 0).  A workgroup owns TOK = 4 consecutive tokens x HG head
-// tiles (one 16-head tile per wave: 4 x 4 = 16 waves at H = 64); wave w handles token
+// bf16 fast path (D % 64 == 0).  A workgroup owns TOK = 2 consecutive tokens x HG head
+// tiles (one 16-head tile per wave: 2 x 4 = 8 waves at H = 64); wave w handles token
 // w / HG and head tile w % HG.  D is walked in stages of 64 elements (128 bytes of every
 // row).  Per stage the workgroup stages, with direct loads into LDS that each move 8
 // rows x 128 bytes (fully coalesced):
-//   * the key band its tokens span (16-key tiles covering [t0-W+1, t0+3]; from L2),
+//   * the key band its tokens span (16-key tiles covering [t0-W+1, t0+1]; from L2),
 //     double buffered, one stage ahead;
-//   * the queries of its 4 tokens (from HBM), triple buffered, two stages ahead; each
-//     wave's two query loads of a stage are issued between its MFMAs.
+//   * the queries of its 2 tokens, double buffered, one stage ahead; each wave's two
+//     query loads of a stage are issued between its MFMAs.
 // Rows are stored with their 16-byte segments XOR-swizzled by (row >> 1) & 7, so the
-// 16-row MFMA fragment reads hit distinct LDS banks.  Loads retire in order, so each
-// stage ends with a counted wait that leaves only the farthest query stage in flight.
-// Every wave computes the same NBT tiles from its first window tile; keys outside the
-// token's window are masked, so the loop has no branches.
-constexpr int kTokMfma = 4;
+// 16-row MFMA fragment reads hit distinct LDS banks.  A workgroup needs about 73 KB of
+// LDS at W = 128, so two share a CU and each covers the other's load waits; it also
+// leaves room for a workgroup of the kernel that follows (the stage loop ends every
+// stage with a full wait and a bare barrier).  Every wave computes the same NBT tiles
+// from its first window tile; keys outside the token's window are masked, so the loop
+// has no branches.
+constexpr int kTokMfma = 2;
 
 __device__ __forceinline__ uint32_t sw_pos(int r, int x) {  // byte offset of row r, segment x
     return (uint32_t)(r * 128 + ((x ^ ((r >> 1) & 7)) << 4));
@@ -189,8 +191,8 @@ __global__ __launch_bounds__(1024) void window_lse_mfma_kernel(
     const int band_bytes = nballoc * 16 * 128;
     const int qst_bytes = kTokMfma * HP * 128;
     unsigned char *band = smem;                   // [2][nballoc*16 rows][128 B]
-    unsigned char *qst = smem + 2 * band_bytes;   // [3][TOK*HP rows][128 B]
-    int32_t *segband = reinterpret_cast<int32_t *>(qst + 3 * qst_bytes);  // [nballoc*16]
+    unsigned char *qst = smem + 2 * band_bytes;   // [2][TOK*HP rows][128 B]
+    int32_t *segband = reinterpret_cast<int32_t *>(qst + 2 * qst_bytes);  // [nballoc*16]
 
     const rsrc_t kr = make_rsrc(reinterpret_cast<const char *>(kwin) + (size_t)b * S * D * 2, (uint32_t)((size_t)S * D * 2));
     const int nqtok = min(kTokMfma, S - t0);
@@ -209,10 +211,10 @@ __global__ __launch_bounds__(1024) void window_lse_mfma_kernel(
         }
     };
     // Queries of D stage st into query buffer st%3; row = tok*HP + head.
-    // Each wave issues exactly two of the TOK*HP/8 = 8*HG instructions (8*HG / (4*HG)
-    // waves): k = 0, 1.
+    // Each wave issues exactly two of the TOK*HP/8 = 2*TOK*HG instructions (there are
+    // TOK*HG waves): k = 0, 1.
     auto stage_q_one = [&](int st, int k) {
-        unsigned char *dst = qst + (st % 3) * qst_bytes;
+        unsigned char *dst = qst + (st & 1) * qst_bytes;
         const int m = w + k * nwaves;
         const int r = 8 * m + r_in;
         const int x = (lane & 7) ^ ((r >> 1) & 7);
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(1024) void window_lse_mfma_kernel(
     // memory pipeline spread over the stage instead of as one burst after the barrier.
     auto compute = [&](int st, int qst_next) {
         const unsigned char *bsrc = band + (st & 1) * band_bytes;
-        const unsigned char *qsrc = qst + (st % 3) * qst_bytes;
+        const unsigned char *qsrc = qst + (st & 1) * qst_bytes;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int x = 4 * c + (lane >> 4);
@@ -273,24 +275,15 @@ __global__ __launch_bounds__(1024) void window_lse_mfma_kernel(
 
     const int nst = D >> 6;
     stage_q(0);
-    if (nst > 1) stage_q(1);
     stage_band(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int st = 0; st < nst; ++st) {
         if (st + 1 < nst) stage_band(st + 1);
-        const bool far = st + 2 < nst;
-        compute(st, far ? st + 2 : -1);  // issues the far query stage (after the band loads)
-        if (far) {
-            // wait for everything but this wave's two far query loads
-            __builtin_amdgcn_s_waitcnt((2 & 0xF) | (0x7 << 4) | (0xF << 8));
-        } else {
-            __builtin_amdgcn_s_waitcnt(0);
-        }
-        // A plain s_barrier: the counted wait above has landed this wave's share of the next
-        // stage, and its LDS reads of this stage were consumed by its MFMAs.  (__syncthreads
-        // adds a workgroup release fence, i.e. vmcnt(0), which would also drain the far
-        // query stage.)
+        compute(st, st + 1 < nst ? st + 1 : -1);  // issues the next query stage between the MFMAs
+        // This wave's share of the next stage has landed in LDS and its reads of this stage
+        // were consumed by its MFMAs; a bare barrier then publishes the stage.
+        __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
     }
     if (!active) return;
@@ -328,7 +321,7 @@ hipError_t launch_mfma(const void *q, const void *kwin, const float *sink, const
                        int D, int W, float scale, float *nc_lse, hipStream_t stream) {
     const int HG = (H + 15) / 16;
     const int nballoc = std::max(win_tiles(W + kTokMfma - 1), NBT + 1);
-    const size_t lds = (size_t)2 * nballoc * 16 * 128 + (size_t)3 * kTokMfma * HG * 16 * 128 + (size_t)nballoc * 16 * 4;
+    const size_t lds = (size_t)2 * nballoc * 16 * 128 + (size_t)2 * kTokMfma * HG * 16 * 128 + (size_t)nballoc * 16 * 4;
     auto kfn = &window_lse_mfma_kernel<NBT>;
     if (lds > 65536) {  // opt in to more than 64 KiB of LDS per workgroup (gfx950 has 160 KiB per CU)
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kfn),
@@ -385,7 +378,7 @@ hipError_t launch1(const void *q, const void *kwin, const float *sink, const int
 hipError_t launch_window_lse(const void *q, const void *kwin, const float *sink, const int32_t *seg, int B,
                              int S, int H, int D, int W, float scale, int dtype, float *nc_lse,
                              hipStream_t stream) {
-    if (dtype == 0 && D % 64 == 0)  // bf16 fast path: 4 tokens x up to 4 head tiles per workgroup
+    if (dtype == 0 && D % 64 == 0)  // bf16 fast path: 2 tokens x up to 4 head tiles per workgroup
         return launch_mfma_w(q, kwin, sink, seg, B, S, H, D, W, scale, nc_lse, stream);
     if (dtype == 0) return launch1<0>(q, kwin, sink, seg, B, S, H, D, W, scale, nc_lse, stream);
     return launch1<1>(q, kwin, sink, seg, B, S, H, D, W, scale, nc_lse, stream);

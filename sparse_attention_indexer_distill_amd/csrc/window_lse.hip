@@ -159,9 +159,8 @@ __global__ __launch_bounds__(kWinTok * 64) void window_lse_kernel(
 //     query loads of a stage are issued between its MFMAs.
 // Rows are stored with their 16-byte segments XOR-swizzled by (row >> 1) & 7, so the
 // 16-row MFMA fragment reads hit distinct LDS banks.  A workgroup needs about 73 KB of
-// LDS at W = 128, so two share a CU and each covers the other's load waits; it also
-// leaves room for a workgroup of the kernel that follows (the stage loop ends every
-// stage with a full wait and a bare barrier).  Every wave computes the same NBT tiles
+// LDS at W = 128, so two share a CU and each covers the other's load waits (the stage
+// loop ends every stage with a full wait and a bare barrier).  Every wave computes the same NBT tiles
 // from its first window tile; keys outside the token's window are masked, so the loop
 // has no branches.
 constexpr int kTokMfma = 2;

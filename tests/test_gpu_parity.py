@@ -168,6 +168,34 @@ def test_shuffled_padding_parity(fused):
     run_config("c2", shuffle_pad=True, fused=fused)
 
 
+def test_fused_without_nc_out_and_floor_options():
+    """distill_target_fused: the target is bitwise the same with and without the optional
+    nc_lse output, its nc_lse matches window_lse within the nc tolerance, and the legacy
+    1e-10 floor clips local-dominant rows exactly as on the three-call path."""
+    sd = _sd()
+    dev = _dev()
+    for name in ("c2", "c1_local"):
+        x = synth.make_inputs(name, shuffle_pad=True)
+        c = x["cfg"]
+        g = _to(x, dev)
+        _say(f"[gpu] {name}: fused options")
+        T1, nc1 = sd.distill_target_fused(g["q"], g["kwin"], g["pool"], g["idx"], g["sink"], g["seg"], W=c.W,
+                                          want_nc=True)
+        T2 = sd.distill_target_fused(g["q"], g["kwin"], g["pool"], g["idx"], g["sink"], g["seg"], W=c.W)
+        nc3 = sd.window_lse(g["q"], g["kwin"], g["sink"], g["seg"], W=c.W)
+        Tl = sd.distill_target_fused(g["q"], g["kwin"], g["pool"], g["idx"], g["sink"], g["seg"], W=c.W,
+                                     l1_floor=1e-10)
+        Tl3 = sd.distill_target(g["q"], g["pool"], g["idx"], nc3, l1_floor=1e-10)
+        torch.cuda.synchronize()
+        assert torch.equal(T1, T2)
+        check_nc(_np(nc1).reshape(-1, c.H), _np(nc3).reshape(-1, c.H).astype(np.float64), name + " fused nc")
+        idx = x["idx"].reshape(-1, c.K).numpy()
+        Tl_ref = oracle.target(x["q"], x["pool"], x["idx"], x["kwin"], x["sink"], x["seg"], W=c.W, scale=c.scale,
+                               floor=1e-10)
+        check_T(_np(Tl).reshape(-1, c.K), Tl_ref, idx, c.N, name + " fused 1e-10 floor")
+        check_T(_np(Tl3).reshape(-1, c.K), Tl_ref, idx, c.N, name + " 3-call 1e-10 floor")
+
+
 # ------------------------------------------------------------------ isolated kernels
 def test_target_isolated_with_given_nc_lse_and_legacy():
     sd = _sd()

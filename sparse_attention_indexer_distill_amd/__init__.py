@@ -97,6 +97,27 @@ def _dev(t: torch.Tensor, name: str, device: torch.device) -> torch.Tensor:
     return t if t.is_contiguous() else t.contiguous()
 
 
+def _out(t: torch.Tensor, name: str, shape, device: torch.device) -> torch.Tensor:
+    """A caller-provided output buffer: float32, contiguous, of the given shape, on device
+    (the kernels write it in place, so it is never copied)."""
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a GPU tensor on {device}")
+    if tuple(t.shape) != tuple(shape) or t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 {list(shape)} tensor")
+    return t
+
+
+def _workspace(t: Optional[torch.Tensor], need: int, device: torch.device) -> torch.Tensor:
+    """Caller-provided scratch (any dtype, contiguous, on device, at least need bytes), or a new one."""
+    if t is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    if not t.is_cuda or t.device != device or not t.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous GPU tensor on {device}")
+    if t.numel() * t.element_size() < need:
+        raise ValueError(f"workspace holds {t.numel() * t.element_size()} bytes, {need} needed")
+    return t
+
+
 def _stream(device: torch.device, stream) -> int:
     s = torch.cuda.current_stream(device) if stream is None else stream
     return s.cuda_stream
@@ -127,8 +148,8 @@ def window_lse(q: torch.Tensor, kwin: torch.Tensor, sink: Optional[torch.Tensor]
             raise ValueError(f"seg must be [{B},{S}]")
     if out is None:
         out = torch.empty((B, S, H), dtype=torch.float32, device=dev)
-    elif out.shape != (B, S, H) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B,S,H] tensor")
+    else:
+        _out(out, "out", (B, S, H), dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     st = lib.window_lse(_ptr(q), _ptr(kwin), _ptr(sink), _ptr(seg), B, S, H, D, int(W), scale,
                         _dtype_code(q), _ptr(out), _stream(dev, stream))
@@ -159,8 +180,8 @@ def distill_target(q: torch.Tensor, pool: torch.Tensor, idx: torch.Tensor,
             raise ValueError(f"nc_lse must be [{B},{S},{H}]")
     if out is None:
         out = torch.empty((B, S, K), dtype=torch.float32, device=dev)
-    elif out.shape != (B, S, K) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B,S,K] tensor")
+    else:
+        _out(out, "out", (B, S, K), dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     st = lib.distill_target(_ptr(q), _ptr(pool), _ptr(idx), _ptr(nc_lse), B, S, H, D, N, K, scale,
                             float(l1_floor), _dtype_code(q), _ptr(out), _stream(dev, stream))
@@ -200,13 +221,12 @@ def distill_target_fused(q: torch.Tensor, kwin: torch.Tensor, pool: torch.Tensor
             raise ValueError(f"seg must be [{B},{S}]")
     if out is None:
         out = torch.empty((B, S, K), dtype=torch.float32, device=dev)
-    elif out.shape != (B, S, K) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [B,S,K] tensor")
+    else:
+        _out(out, "out", (B, S, K), dev)
     if nc_out is None and want_nc:
         nc_out = torch.empty((B, S, H), dtype=torch.float32, device=dev)
-    if nc_out is not None and (nc_out.shape != (B, S, H) or nc_out.dtype != torch.float32
-                               or not nc_out.is_contiguous()):
-        raise ValueError("nc_out must be a contiguous float32 [B,S,H] tensor")
+    if nc_out is not None:
+        _out(nc_out, "nc_out", (B, S, H), dev)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     st = lib.distill_target_fused(_ptr(q), _ptr(kwin), _ptr(sink), _ptr(seg), _ptr(pool), _ptr(idx), B, S, H, D, N,
                                   K, int(W), scale, float(l1_floor), _dtype_code(q), _ptr(out), _ptr(nc_out),
@@ -237,17 +257,16 @@ def distill_kl_fwd_bwd(target: torch.Tensor, logits: torch.Tensor, idx: torch.Te
         raise ValueError("target and logits must be float32")
     idx = _dev(idx.to(torch.int32), "idx", dev)
     B, S, K = target.shape
-    if kl_rows is None:
-        kl_rows = torch.empty((B, S), dtype=torch.float32, device=dev)
-    if want_grad and dlogits is None:
-        dlogits = torch.empty((B, S, K), dtype=torch.float32, device=dev)
+    kl_rows = torch.empty((B, S), dtype=torch.float32, device=dev) if kl_rows is None else \
+        _out(kl_rows, "kl_rows", (B, S), dev)
     if not want_grad:
         dlogits = None
-    if stats is None:
-        stats = torch.empty(2, dtype=torch.float32, device=dev)
-    need = distill_kl_workspace_bytes(B, S, K)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif dlogits is None:
+        dlogits = torch.empty((B, S, K), dtype=torch.float32, device=dev)
+    else:
+        _out(dlogits, "dlogits", (B, S, K), dev)
+    stats = torch.empty(2, dtype=torch.float32, device=dev) if stats is None else _out(stats, "stats", (2,), dev)
+    workspace = _workspace(workspace, distill_kl_workspace_bytes(B, S, K), dev)
     st = lib.distill_kl_fwd_bwd(_ptr(target), _ptr(logits), _ptr(idx), B, S, K, int(N), float(grad_scale),
                                 _ptr(kl_rows), _ptr(dlogits), _ptr(stats), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(dev, stream))

@@ -465,3 +465,46 @@ def test_binding_rejects_bad_arguments_on_gpu_tensors():
         sd.window_lse(q, k, None, None, W=0)
     with pytest.raises(NotImplementedError):
         sd.window_lse(q, k, None, None, W=129)
+
+
+def test_binding_rejects_bad_output_buffers():
+    """Caller-provided outputs and workspaces are written in place, so the binding refuses
+    any that is on the host, of the wrong shape or dtype, non-contiguous or too small,
+    before anything is launched."""
+    sd = _sd()
+    dev = _dev()
+    B, S, H, D, N, K = 1, 16, 4, 64, 4, 4
+    q = torch.zeros(B, S, H, D, dtype=torch.bfloat16, device=dev)
+    k = torch.zeros(B, S, D, dtype=torch.bfloat16, device=dev)
+    pool = torch.zeros(B, N, D, dtype=torch.bfloat16, device=dev)
+    idx = torch.full((B, S, K), -1, dtype=torch.int32, device=dev)
+    bad_nc = [torch.empty(B, S, H),                                         # host
+              torch.empty(B, S, H + 1, device=dev),                         # shape
+              torch.empty(B, S, H, dtype=torch.float64, device=dev),        # dtype
+              torch.empty(B, H, S, device=dev).transpose(1, 2)]             # non-contiguous
+    for out in bad_nc:
+        with pytest.raises(ValueError):
+            sd.window_lse(q, k, None, None, W=4, out=out)
+        with pytest.raises(ValueError):
+            sd.distill_target_fused(q, k, pool, idx, None, None, W=4, nc_out=out)
+    for out in (torch.empty(B, S, K), torch.empty(B, S, K + 1, device=dev)):
+        with pytest.raises(ValueError):
+            sd.distill_target(q, pool, idx, None, out=out)
+        with pytest.raises(ValueError):
+            sd.distill_target_fused(q, k, pool, idx, None, None, W=4, out=out)
+    T = torch.zeros(B, S, K, device=dev)
+    z = torch.zeros(B, S, K, device=dev)
+    with pytest.raises(ValueError):
+        sd.distill_kl_fwd_bwd(T, z, idx, N, stats=torch.empty(3, device=dev))
+    with pytest.raises(ValueError):
+        sd.distill_kl_fwd_bwd(T, z, idx, N, kl_rows=torch.empty(B, S))
+    with pytest.raises(ValueError):
+        sd.distill_kl_fwd_bwd(T, z, idx, N, dlogits=torch.empty(B, S, K - 1, device=dev))
+    with pytest.raises(ValueError):
+        sd.distill_kl_fwd_bwd(T, z, idx, N, workspace=torch.empty(1, dtype=torch.uint8, device=dev))
+    with pytest.raises(ValueError):
+        sd.distill_kl_fwd_bwd(T, z, idx, N, workspace=torch.empty(64, dtype=torch.uint8))
+    # valid calls still go through after the rejections
+    kl, dz, st = sd.distill_kl_fwd_bwd(T, z, idx, N)
+    torch.cuda.synchronize()
+    assert st.tolist() == [0.0, 0.0] and (kl == 0).all() and (dz == 0).all()

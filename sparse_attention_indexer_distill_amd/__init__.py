@@ -118,6 +118,17 @@ def _workspace(t: Optional[torch.Tensor], need: int, device: torch.device) -> to
     return t
 
 
+def _slots(idx: torch.Tensor, N: int, device: torch.device) -> torch.Tensor:
+    """Top-k slots as int32 on device.  Wider integer slots are mapped to -1 outside [0, N)
+    before the cast (asynchronously, on the device), so no value can wrap into a valid row."""
+    if idx.dtype == torch.int32:
+        return _dev(idx, "idx", device)
+    if idx.dtype not in (torch.int64, torch.int16, torch.uint8, torch.int8):
+        raise ValueError(f"idx must be an integer tensor, got {idx.dtype}")
+    idx = _dev(idx, "idx", device)
+    return torch.where((idx >= 0) & (idx < N), idx, torch.full_like(idx, -1)).to(torch.int32)
+
+
 def _stream(device: torch.device, stream) -> int:
     s = torch.cuda.current_stream(device) if stream is None else stream
     return s.cuda_stream
@@ -172,7 +183,7 @@ def distill_target(q: torch.Tensor, pool: torch.Tensor, idx: torch.Tensor,
     N = pool.shape[1]
     if idx.dim() != 3 or idx.shape[:2] != (B, S):
         raise ValueError(f"idx must be [{B},{S},K]")
-    idx = _dev(idx.to(torch.int32), "idx", dev)
+    idx = _slots(idx, N, dev)
     K = idx.shape[2]
     if nc_lse is not None:
         nc_lse = _dev(nc_lse.detach().to(torch.float32), "nc_lse", dev)
@@ -209,7 +220,7 @@ def distill_target_fused(q: torch.Tensor, kwin: torch.Tensor, pool: torch.Tensor
     N = pool.shape[1]
     if idx.dim() != 3 or idx.shape[:2] != (B, S):
         raise ValueError(f"idx must be [{B},{S},K]")
-    idx = _dev(idx.to(torch.int32), "idx", dev)
+    idx = _slots(idx, N, dev)
     K = idx.shape[2]
     if sink is not None:
         sink = _dev(sink.detach().to(torch.float32), "sink", dev)
@@ -255,7 +266,7 @@ def distill_kl_fwd_bwd(target: torch.Tensor, logits: torch.Tensor, idx: torch.Te
         raise ValueError("target, logits and idx must share one [B,S,K] shape")
     if target.dtype != torch.float32 or logits.dtype != torch.float32:
         raise ValueError("target and logits must be float32")
-    idx = _dev(idx.to(torch.int32), "idx", dev)
+    idx = _slots(idx, int(N), dev)
     B, S, K = target.shape
     kl_rows = torch.empty((B, S), dtype=torch.float32, device=dev) if kl_rows is None else \
         _out(kl_rows, "kl_rows", (B, S), dev)

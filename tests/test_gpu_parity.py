@@ -508,3 +508,32 @@ def test_binding_rejects_bad_output_buffers():
     kl, dz, st = sd.distill_kl_fwd_bwd(T, z, idx, N)
     torch.cuda.synchronize()
     assert st.tolist() == [0.0, 0.0] and (kl == 0).all() and (dz == 0).all()
+
+
+def test_int64_slots_outside_range_never_wrap_into_valid_rows():
+    """An int64 slot such as 2^32 + 1 must stay invalid (it would read as row 1 if it were
+    simply cast to int32): target, KL and gradient equal those of the same row with -1."""
+    sd = _sd()
+    dev = _dev()
+    x = synth.make_inputs("c2")
+    c = x["cfg"]
+    g = _to(x, dev)
+    idx64 = g["idx"].to(torch.int64)
+    ref_idx = g["idx"].clone()
+    t = c.S - 1                                   # a full row: every slot valid
+    idx64[0, t, 0] = (1 << 32) + 1
+    idx64[0, t, 1] = -(1 << 33)
+    ref_idx[0, t, 0] = -1
+    ref_idx[0, t, 1] = -1
+    _say("[gpu] c2: int64 slots")
+    nc = sd.window_lse(g["q"], g["kwin"], g["sink"], g["seg"], W=c.W)
+    T64 = sd.distill_target(g["q"], g["pool"], idx64, nc)
+    Tref = sd.distill_target(g["q"], g["pool"], ref_idx, nc)
+    Tf64 = sd.distill_target_fused(g["q"], g["kwin"], g["pool"], idx64, g["sink"], g["seg"], W=c.W)
+    Tfref = sd.distill_target_fused(g["q"], g["kwin"], g["pool"], ref_idx, g["sink"], g["seg"], W=c.W)
+    kl64, dz64, st64 = sd.distill_kl_fwd_bwd(Tref, g["z"], idx64, c.N)
+    klr, dzr, str_ = sd.distill_kl_fwd_bwd(Tref, g["z"], ref_idx, c.N)
+    torch.cuda.synchronize()
+    assert torch.equal(T64, Tref) and torch.equal(Tf64, Tfref)
+    assert torch.equal(kl64, klr) and torch.equal(dz64, dzr) and torch.equal(st64, str_)
+    assert T64[0, t, 0] == 0 and T64[0, t, 1] == 0

@@ -433,8 +433,8 @@ struct TargetArgs {
 // Window part of the joint softmax for token t of batch b, inside the target kernel:
 // the LSE over {scale <q_h, kwin_j> : j in [max(0, t-W+1), t], seg[j] == seg[t]} plus the
 // sink, per head.  Window tiles of 16 consecutive keys starting at the first key are dealt
-// to the waves like slot tiles (at most KWT per wave) and scored with the same MFMA loop
-// against the staged queries.  window_local publishes each wave's masked per-head maximum
+// in pairs: wave w scores tiles 2w and 2w+1 together in one pass of the same MFMA loop, so
+// each pair reads the staged queries once (half the query reads of one tile per wave).  window_local publishes each wave's masked per-head maximum
 // and sum in red_wm/red_ws without waiting; after the epilogue's barrier window_combine
 // reduces them over the waves and adds the sink, returning in natural log the value of head
 // 16*min(g, HT-1) + x for lane (g, x) -- the layout the epilogue takes its nc values in.
@@ -444,8 +444,8 @@ __device__ __forceinline__ void window_local(const TargetArgs &a, const unsigned
     constexpr int EB = Elem<DT>::bytes;
     const int S = a.S, D = a.D, nch = D >> 5;
     const int kf = t - a.W + 1 > 0 ? t - a.W + 1 : 0;
-    const int nwt = (t - kf + 16) >> 4;
-    const int myw = nwt > w ? (nwt - w + NW - 1) / NW : 0;
+    const int nwt = (t - kf + 16) >> 4;                                 // at most 8 (W <= 128)
+    const int myw = nwt - 2 * w >= 2 ? 2 : (nwt - 2 * w > 0 ? nwt - 2 * w : 0);  // tiles 2w, 2w+1
     const rsrc_t kr = make_rsrc(reinterpret_cast<const char *>(a.kwin) + (size_t)b * S * D * EB,
                                 (uint32_t)((size_t)S * D * EB));
     f32x4 acc[KWT][HT];
@@ -459,14 +459,14 @@ __device__ __forceinline__ void window_local(const TargetArgs &a, const unsigned
         uint32_t off[KWT];
 #pragma unroll
         for (int l = 0; l < KWT; ++l) {
-            int r = kf + 16 * (w + l * NW) + (DT == 0 ? (int)quad_row_lane(lane) : (lane & 15));
+            int r = kf + 16 * (2 * w + l) + (DT == 0 ? (int)quad_row_lane(lane) : (lane & 15));
             r = r < t ? r : t;  // rows past t are loaded as row t and masked below
             off[l] = DT == 0 ? (uint32_t)(r * D * EB) + quad_seg_bytes(lane)
                              : (uint32_t)((r * D + 8 * (lane >> 4)) * EB);
         }
         score_dispatch<DT, HT, KWT>(myw, acc, qb, RS, kr, off, nch, 0, lane);
     }
-    // masked statistics (log2 domain); key j of element (l, i) = kf + 16(w + l*NW) + 4g + i
+    // masked statistics (log2 domain); key j of element (l, i) = kf + 16(2w + l) + 4g + i
     const int x = lane & 15, g = lane >> 4;
     const int sg_t = a.seg ? a.seg[(size_t)b * S + t] : 0;
     bool okj[KWT][4];
@@ -474,7 +474,7 @@ __device__ __forceinline__ void window_local(const TargetArgs &a, const unsigned
     for (int l = 0; l < KWT; ++l)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int j = kf + 16 * (w + l * NW) + 4 * g + i;
+            const int j = kf + 16 * (2 * w + l) + 4 * g + i;
             okj[l][i] = l < myw && j <= t && (a.seg == nullptr || a.seg[(size_t)b * S + j] == sg_t);
         }
 #pragma unroll
@@ -526,7 +526,8 @@ template <int DT, int HT, int KT, int NW, bool FUSED>
 __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kernel(const TargetArgs a) {
     constexpr int EB = Elem<DT>::bytes;
     constexpr int KP = 2;                      // slot passes of NW*64 (K <= 2*NW*64)
-    constexpr int KWT = (8 + NW - 1) / NW;     // window tiles per wave (W <= 128)
+    constexpr int KWT = 2;                     // window tiles per wave (W <= 128, NW >= 4)
+    static_assert(!FUSED || NW >= 4, "the eight window tiles need four waves at two tiles each");
     extern __shared__ __align__(16) unsigned char smem[];
     const int S = a.S, H = a.H, D = a.D, N = a.N, K = a.K;
     const int nch = D >> 5;

@@ -315,6 +315,10 @@ EDGE = [
     ("persist_b2_h20", 2, 600, 20, 512, 150, 300, 33, "bf16", 1),
     ("persist_b3_h64", 3, 400, 64, 512, 100, 512, 64, "bf16", 2),
     ("persist_k16_h5", 1, 1024, 5, 512, 256, 16, 40, "bf16", 1),
+    # four waves per token (K <= 256) holding all eight window tiles two to a wave; W = 120
+    # leaves the last window tile partly masked, across two segments
+    ("w128_four_waves", 1, 300, 16, 128, 75, 64, 128, "bf16", 1),
+    ("w120_four_waves_seg", 1, 264, 8, 64, 66, 200, 120, "bf16", 2),
 ]
 
 

@@ -69,7 +69,8 @@ enum { SD_BF16 = 0, SD_F32 = 1 };
  *   seg    [B,S]      int32 or NULL   packed-segment ids; NULL = one segment
  *   nc_lse [B,S,H]    float32 out     natural-log mass (never -inf: j = t is in win(t))
  * Limits: D % 32 == 0, D <= 512; H <= 64; 1 <= W <= 128; S * D * element size < 2^31
- * bytes (one batch row of kwin).
+ * bytes (one batch row of kwin); S <= 2^24 - 2 (the grid has one 512-lane workgroup per
+ * two tokens, and a dispatch counts at most 2^32 - 1 work-items).
  */
 int window_lse(const void *q, const void *kwin, const float *sink, const int32_t *seg,
                int B, int S, int H, int D, int W, float scale, int dtype, float *nc_lse,
@@ -100,7 +101,8 @@ int window_lse(const void *q, const void *kwin, const float *sink, const int32_t
  *   l1_floor         <= 0 selects FLT_MIN (2^-126); 1e-10 reproduces the legacy floor
  *   target [B,S,K]   float32 out      a row with no valid slot is all zeros
  * Limits: D % 32 == 0, D <= 512; H <= 64; K <= 1024; N * D * element size < 2^31 bytes
- * (one batch row of pool).  A non-positive or non-finite scale is rejected with
+ * (one batch row of pool); B * S < 2^22 (one workgroup of up to 1024 lanes per token, and a
+ * dispatch counts at most 2^32 - 1 work-items).  A non-positive or non-finite scale is rejected with
  * SD_ERR_BAD_SHAPE.
  */
 int distill_target(const void *q, const void *pool, const int32_t *idx, const float *nc_lse,
@@ -153,7 +155,8 @@ int distill_target_fused(const void *q, const void *kwin, const float *sink, con
  *   workspace: device scratch of distill_kl_workspace_bytes(B,S,K) bytes, 16-byte
  *   aligned, owned by the caller; its contents need no initialisation and are
  *   overwritten.  Calls that share a workspace must be ordered (same stream).
- * Limits: K <= 4096.
+ * Limits: K <= 4096; B * S <= 2^26 - 8 (one 512-lane workgroup per 8 rows, and a dispatch
+ * counts at most 2^32 - 1 work-items).
  */
 size_t distill_kl_workspace_bytes(int B, int S, int K);
 int distill_kl_fwd_bwd(const float *target, const float *logits, const int32_t *idx,

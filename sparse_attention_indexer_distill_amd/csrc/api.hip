@@ -53,6 +53,16 @@ int check_rows(const char *fn, const char *what, int64_t rows, int D, int dtype)
     return SD_OK;
 }
 
+// A dispatch counts its grid in work-items with 32-bit sizes, so blocks * threads per
+// block must stay at or below 2^32 - 1.  The limits are checked here, before any HIP call,
+// with the widest workgroup each entry point can launch.
+int check_grid(const char *fn, int64_t blocks, int threads, const char *limit) {
+    if (blocks * threads > (int64_t)UINT32_MAX)
+        return fail(SD_ERR_UNSUPPORTED, "%s: %s (the grid would hold %lld work-items, above 2^32 - 1)", fn, limit,
+                    (long long)(blocks * threads));
+    return SD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -80,6 +90,7 @@ int window_lse(const void *q, const void *kwin, const float *sink, const int32_t
     if (W > sd::kMaxWindow) return fail(SD_ERR_UNSUPPORTED, "window_lse: W=%d exceeds %d", W, sd::kMaxWindow);
     if (!isfinite(scale)) return fail(SD_ERR_BAD_SHAPE, "window_lse: scale must be finite");
     if ((st = check_rows("window_lse", "kwin", S, D, dtype)) != SD_OK) return st;
+    if ((st = check_grid("window_lse", ((int64_t)S + 1) / 2, 512, "S must be at most 2^24 - 2")) != SD_OK) return st;
     return hip_status(sd::launch_window_lse(q, kwin, sink, seg, B, S, H, D, W, scale, dtype, nc_lse, stream),
                       "window_lse launch");
 }
@@ -95,6 +106,7 @@ int distill_target(const void *q, const void *pool, const int32_t *idx, const fl
     if (!isfinite(scale) || !(scale > 0.f) || isnan(l1_floor))
         return fail(SD_ERR_BAD_SHAPE, "distill_target: scale must be positive and finite, l1_floor not NaN");
     if ((st = check_rows("distill_target", "pool", N, D, dtype)) != SD_OK) return st;
+    if ((st = check_grid("distill_target", (int64_t)B * S, 1024, "B*S must be below 2^22")) != SD_OK) return st;
     return hip_status(sd::launch_distill_target(q, pool, idx, nc_lse, B, S, H, D, N, K, scale, l1_floor, dtype,
                                                 target, stream),
                       "distill_target launch");
@@ -115,6 +127,8 @@ int distill_target_fused(const void *q, const void *kwin, const float *sink, con
         return fail(SD_ERR_BAD_SHAPE, "distill_target_fused: scale must be positive and finite, l1_floor not NaN");
     if ((st = check_rows("distill_target_fused", "pool", N, D, dtype)) != SD_OK) return st;
     if ((st = check_rows("distill_target_fused", "kwin", S, D, dtype)) != SD_OK) return st;
+    if ((st = check_grid("distill_target_fused", (int64_t)B * S, 1024, "B*S must be below 2^22")) != SD_OK)
+        return st;
     return hip_status(sd::launch_distill_target_fused(q, kwin, sink, seg, pool, idx, B, S, H, D, N, K, W, scale,
                                                       l1_floor, dtype, target, nc_lse_out, stream),
                       "distill_target_fused launch");
@@ -133,8 +147,8 @@ int distill_kl_fwd_bwd(const float *target, const float *logits, const int32_t *
     if (B <= 0 || S <= 0 || K <= 0 || N <= 0)
         return fail(SD_ERR_BAD_SHAPE, "distill_kl_fwd_bwd: sizes must be positive (B=%d S=%d K=%d N=%d)", B, S, K, N);
     if (K > sd::kMaxKlK) return fail(SD_ERR_UNSUPPORTED, "distill_kl_fwd_bwd: K=%d exceeds %d", K, sd::kMaxKlK);
-    if ((int64_t)B * S > ((int64_t)1 << 31) - 4)
-        return fail(SD_ERR_UNSUPPORTED, "distill_kl_fwd_bwd: B*S too large");
+    int st = check_grid("distill_kl_fwd_bwd", ((int64_t)B * S + 7) / 8, 512, "B*S must be at most 2^26 - 8");
+    if (st != SD_OK) return st;
     if (!isfinite(grad_scale)) return fail(SD_ERR_BAD_SHAPE, "distill_kl_fwd_bwd: grad_scale must be finite");
     const size_t need = sd::kl_workspace_bytes(B, S, K);
     if (workspace_bytes < need)

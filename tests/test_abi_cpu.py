@@ -75,6 +75,9 @@ def test_window_lse_rejections(lib):
     assert _wl(lib, S=1 << 21, D=512) == sd.SD_ERR_UNSUPPORTED            # exactly 2^31 bytes of bf16
     assert b"2^31" in lib.sd_last_error()
     assert _wl(lib, S=1 << 20, D=512, dtype=1) == sd.SD_ERR_UNSUPPORTED   # fp32
+    # a dispatch counts at most 2^32 - 1 work-items: 512 lanes per two tokens
+    assert _wl(lib, S=(1 << 24) - 1, D=32) == sd.SD_ERR_UNSUPPORTED       # kwin row 2^30 bytes: fine
+    assert b"2^32 - 1" in lib.sd_last_error()
 
 
 def _tg(lib, q=FAKE, pool=FAKE, idx=FAKE, out=FAKE, B=1, S=8, H=4, D=32, N=2, K=4, scale=0.1, floor=0.0, dtype=0):
@@ -98,6 +101,10 @@ def test_distill_target_rejections(lib):
     assert _tg(lib, H=128) == sd.SD_ERR_UNSUPPORTED
     assert _tg(lib, N=1 << 21, D=512) == sd.SD_ERR_UNSUPPORTED           # pool row of 2^31 bytes
     assert b"pool" in lib.sd_last_error()
+    # up to 1024 lanes per token: B*S must stay below 2^22
+    assert _tg(lib, B=1, S=1 << 22, H=1) == sd.SD_ERR_UNSUPPORTED
+    assert b"2^22" in lib.sd_last_error()
+    assert _tg(lib, B=4, S=1 << 20, H=1) == sd.SD_ERR_UNSUPPORTED
 
 
 def _tf(lib, q=FAKE, k=FAKE, pool=FAKE, idx=FAKE, out=FAKE, B=1, S=8, H=4, D=32, N=2, K=4, W=4, scale=0.1,
@@ -127,6 +134,8 @@ def test_distill_target_fused_rejections(lib):
     assert b"pool" in lib.sd_last_error()
     assert _tf(lib, S=1 << 21, D=512) == sd.SD_ERR_UNSUPPORTED
     assert b"kwin" in lib.sd_last_error()
+    assert _tf(lib, B=2, S=1 << 21, H=1) == sd.SD_ERR_UNSUPPORTED
+    assert b"2^22" in lib.sd_last_error()
 
 
 def _kl(lib, T=FAKE, z=FAKE, idx=FAKE, B=1, S=8, K=4, N=2, g=1.0, rows=FAKE, dz=FAKE, st=FAKE, ws=FAKE,
@@ -148,6 +157,10 @@ def test_distill_kl_rejections(lib):
     assert _kl(lib, wsb=7) == sd.SD_ERR_BAD_SHAPE  # one 8-row block needs 8 bytes
     assert b"workspace" in lib.sd_last_error()
     assert _kl(lib, K=4097) == sd.SD_ERR_UNSUPPORTED
+    # 512 lanes per 8 rows: B*S at most 2^26 - 8
+    assert _kl(lib, B=1, S=(1 << 26) - 7) == sd.SD_ERR_UNSUPPORTED
+    assert _kl(lib, B=2, S=1 << 25) == sd.SD_ERR_UNSUPPORTED
+    assert b"2^26 - 8" in lib.sd_last_error()
     assert _kl(lib, ws=ctypes.c_void_p(0x1004)) == sd.SD_ERR_BAD_SHAPE   # not 16-byte aligned
 
 

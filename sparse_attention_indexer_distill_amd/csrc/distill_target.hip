@@ -434,10 +434,11 @@ struct TargetArgs {
 // the LSE over {scale <q_h, kwin_j> : j in [max(0, t-W+1), t], seg[j] == seg[t]} plus the
 // sink, per head.  Window tiles of 16 consecutive keys starting at the first key are dealt
 // in pairs: wave w scores tiles 2w and 2w+1 together in one pass of the same MFMA loop, so
-// each pair reads the staged queries once (half the query reads of one tile per wave).  window_local publishes each wave's masked per-head maximum
-// and sum in red_wm/red_ws without waiting; after the epilogue's barrier window_combine
-// reduces them over the waves and adds the sink, returning in natural log the value of head
-// 16*min(g, HT-1) + x for lane (g, x) -- the layout the epilogue takes its nc values in.
+// each pair reads the staged queries once (half the query reads of one tile per wave).
+// window_local publishes each wave's masked per-head maximum and sum in red_wm/red_ws
+// without waiting; after the epilogue's barrier window_combine reduces them over the waves
+// and adds the sink, returning in natural log the value of head 16*min(g, HT-1) + x for
+// lane (g, x) -- the layout the epilogue takes its nc values in.
 template <int DT, int HT, int NW, int KWT>
 __device__ __forceinline__ void window_local(const TargetArgs &a, const unsigned char *qb, int RS, int b, int t, int w,
                                              int lane, float *red_wm, float *red_ws) {

@@ -182,3 +182,11 @@ def test_binding_maps_status_codes_to_exceptions(lib):
         sd._check(sd.SD_ERR_BAD_SHAPE, "x")
     with pytest.raises(RuntimeError):
         sd._check(sd.SD_ERR_HIP, "x")
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built HIP library the binding raises; it has no CPU path to fall back to."""
+    monkeypatch.setattr(sd, "_lib", None)
+    monkeypatch.setattr(sd, "_LIB_PATH", str(tmp_path / "libsparse_distill.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        sd.load_library()

@@ -127,6 +127,55 @@ __device__ __forceinline__ void score_tiles(f32x4 (&acc)[KT][HT], const unsigned
     mma(a1, b1);
 }
 
+// fp32 scores in passes of at most two tiles.  Each head tile's query fragment is read
+// from LDS just before its MFMAs through a two-deep ring, so two tiles' row fragments (double
+// buffered over chunks), two query fragments and the accumulators stay within the 128
+// VGPRs a wave has when 16 waves share a workgroup.
+template <int HT, int MY, int KT>
+__device__ __forceinline__ void score_f32(f32x4 (&acc)[KT][HT], const unsigned char *__restrict__ qb, int RS,
+                                          rsrc_t pool, const uint32_t (&off)[KT], int nch, int lane) {
+    constexpr uint32_t CB = 32 * 4;  // bytes of one 32-element fp32 chunk of a row
+#pragma unroll
+    for (int l0 = 0; l0 < MY; l0 += 2) {
+        f32x8 a0[2], a1[2];
+        auto load = [&](f32x8(&a)[2], int c) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                if (l0 + t < MY) a[t] = buf_load_frag<1>(pool, off[l0 + t] + (uint32_t)c * CB);
+        };
+        auto mma = [&](const f32x8(&a)[2], int c) {
+            f32x8 b[2];
+            b[0] = q_frag<1, HT>(qb, RS, 0, c, lane);
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                if (ht + 1 < HT) b[(ht + 1) & 1] = q_frag<1, HT>(qb, RS, ht + 1, c, lane);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    if (l0 + t < MY) acc[l0 + t][ht] = mfma_frag<1>(a[t], b[ht & 1], acc[l0 + t][ht]);
+            }
+        };
+        load(a0, 0);
+        int c = 0;
+        for (; c + 1 < nch; c += 2) {
+            load(a1, c + 1);
+            mma(a0, c);
+            if (c + 2 < nch) load(a0, c + 2);
+            mma(a1, c + 1);
+        }
+        if (c < nch) mma(a0, c);
+    }
+}
+
+template <int HT, int KT, int MY = KT>
+__device__ __forceinline__ void score_dispatch_f32(int my, f32x4 (&acc)[KT][HT], const unsigned char *__restrict__ qb,
+                                                   int RS, rsrc_t pool, const uint32_t (&off)[KT], int nch, int lane) {
+    if (my == MY) {
+        score_f32<HT, MY, KT>(acc, qb, RS, pool, off, nch, lane);
+    } else if constexpr (MY > 1) {
+        score_dispatch_f32<HT, KT, MY - 1>(my, acc, qb, RS, pool, off, nch, lane);
+    }
+}
+
 // bf16 scores from 128-byte row pieces (two chunks per load pair; see pair_frags).  The
 // tiles are scored PT at a time, so only PT tiles' raw loads and fragments are live next
 // to the accumulators; the next piece's loads are issued as soon as the current one has
@@ -465,7 +514,11 @@ __device__ __forceinline__ void window_local(const TargetArgs &a, const unsigned
             off[l] = DT == 0 ? (uint32_t)(r * D * EB) + quad_seg_bytes(lane)
                              : (uint32_t)((r * D + 8 * (lane >> 4)) * EB);
         }
-        score_dispatch<DT, HT, KWT>(myw, acc, qb, RS, kr, off, nch, 0, lane);
+        if constexpr (DT == 0) {
+            score_dispatch<DT, HT, KWT>(myw, acc, qb, RS, kr, off, nch, 0, lane);
+        } else {
+            score_dispatch_f32<HT, KWT>(myw, acc, qb, RS, kr, off, nch, lane);
+        }
     }
     // masked statistics (log2 domain); key j of element (l, i) = kf + 16(2w + l) + 4g + i
     const int x = lane & 15, g = lane >> 4;
@@ -614,7 +667,7 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
             const int r = (l < my && pos < nv) ? crow[pos] : crow[0];
             off[l] = (uint32_t)((r * D + 8 * (lane >> 4)) * EB);
         }
-        if (my > 0) score_dispatch<DT, HT, KT>(my, acc, qb, RS, pr, off, nch, 0, lane);
+        if (my > 0) score_dispatch_f32<HT, KT>(my, acc, qb, RS, pr, off, nch, lane);
     }
 
     // 3.-6. Epilogue: per-head statistics, joint denominators, head sums, normalised scatter.

@@ -363,6 +363,9 @@ EDGE = [
     # leaves the last window tile partly masked, across two segments
     ("w128_four_waves", 1, 300, 16, 128, 75, 64, 128, "bf16", 1),
     ("w120_four_waves_seg", 1, 264, 8, 64, 66, 200, 120, "bf16", 2),
+    # fp32 inputs on the 16-wave workgroup (K > 512, H > 32) with up to four slot tiles per
+    # wave, scored in passes of two, and all eight window tiles
+    ("f32_h40_k1024", 1, 4200, 40, 32, 1050, 1024, 128, "f32", 1),
 ]
 
 

@@ -53,6 +53,8 @@ def _load():
                                      [ctypes.c_double, ctypes.c_double, _lp, ctypes.c_int64, _dp]
         lib.oracle_kl.argtypes = [_fp, _fp, _ip] + [ctypes.c_int] * 4 + \
                                  [ctypes.c_double, _lp, ctypes.c_int64, _dp, _dp, _dp]
+        lib.oracle_indexer_topk.argtypes = [_fp, _ip] + [ctypes.c_int] * 5 + [_lp, ctypes.c_int64, _ip, _fp]
+        lib.oracle_indexer_topk_bwd.argtypes = [_fp, _ip] + [ctypes.c_int] * 4 + [_lp, ctypes.c_int64, _dp]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = lib
@@ -161,3 +163,34 @@ def kl(T, z, idx, N: int, grad_scale: float = 1.0, rows=None, want_grad: bool = 
                       klo.ctypes.data_as(_dp), dz.ctypes.data_as(_dp) if want_grad else None,
                       st.ctypes.data_as(_dp))
     return klo, dz, st
+
+
+def indexer_topk(scores, seg, K: int, ratio: int, rows=None):
+    """Masked top-k selection of the indexer.  scores [B,S,N] (read as float32), seg [B,S]
+    or None.  Block n is visible to token t iff it is complete at t (ratio*n + ratio - 1
+    <= t) and all its tokens share t's segment id.  The K visible blocks with the largest
+    scores are kept (equal scores: smaller index first; NaN ranks lowest) and returned in
+    ascending block order, then -1.  Returns (idx int32 [nrows,K], values float32 [nrows,K],
+    -inf at -1 slots)."""
+    sa, sp = _f32(scores)
+    B, S, N = sa.shape
+    ga, gp = _i32(seg)
+    ra, rp, n = _rows(rows, B * S)
+    idx = np.empty((n, K), dtype=np.int32)
+    val = np.empty((n, K), dtype=np.float32)
+    _load().oracle_indexer_topk(sp, gp, B, S, N, int(K), int(ratio), rp, n,
+                                idx.ctypes.data_as(_ip), val.ctypes.data_as(_fp))
+    return idx, val
+
+
+def indexer_topk_bwd(dval, idx, N: int, rows=None):
+    """Adjoint of the gather values = scores[idx]: dscores[r, n] = sum of dval over the
+    valid slots holding n (slot order), 0 elsewhere.  dval, idx [B,S,K].  Returns float64
+    [nrows, N]."""
+    da, dp = _f32(dval)
+    ia, ip = _i32(idx)
+    B, S, K = ia.shape
+    ra, rp, n = _rows(rows, B * S)
+    out = np.empty((n, N), dtype=np.float64)
+    _load().oracle_indexer_topk_bwd(dp, ip, B, S, int(N), K, rp, n, out.ctypes.data_as(_dp))
+    return out

@@ -243,3 +243,94 @@ void oracle_kl(const float *T, const float *z, const int32_t *idx, int B, int S,
     stats[0] = s;
     stats[1] = cnt;
 }
+
+/* ----------------------------------------------------------------------------------
+ * Indexer top-k selection, the step before the target ([P3] MaxText PR "Add Indexer Loss
+ * [Deepseek v4]": the indexer keeps the top-k compressed blocks of each query under the
+ * causal block mask combined with the segment (packing) mask -- commit list: "0.0
+ * probability mass on all future blocks", "segment/packing mask"; the t=4 example: block 0
+ * visible, block 1 masked -- and turns the slots it cannot fill into -1, review comment on
+ * jnp.where(invalid, -1, top_k_indices)).
+ *
+ *   block n (tokens ratio*n .. ratio*n + ratio - 1) is visible to token t iff n < N, the
+ *   block is complete at t (ratio*n + ratio - 1 <= t) and every one of its tokens carries
+ *   t's segment id (seg == NULL: one segment).
+ *   Among the visible blocks, the K with the largest score are kept; equal scores prefer
+ *   the smaller block index; a NaN score ranks below every number.  The kept blocks are
+ *   written in ascending block order, then -1 for the slots left over; values[k] is the
+ *   kept block's score, -inf at a -1 slot.
+ * out_idx, out_val: [nrows, K] */
+typedef struct {
+    float s;
+    int32_t n;
+} oracle_cand;
+
+/* a before b in the selection order: larger score first, NaN last, then smaller index */
+static int cand_rank_cmp(const void *pa, const void *pb) {
+    const oracle_cand *a = (const oracle_cand *)pa, *b = (const oracle_cand *)pb;
+    const int na = isnan(a->s), nb = isnan(b->s);
+    if (na != nb) return na ? 1 : -1;
+    if (!na && a->s != b->s) return a->s > b->s ? -1 : 1;
+    return a->n < b->n ? -1 : (a->n > b->n ? 1 : 0);
+}
+
+static int cand_index_cmp(const void *pa, const void *pb) {
+    const oracle_cand *a = (const oracle_cand *)pa, *b = (const oracle_cand *)pb;
+    return a->n < b->n ? -1 : (a->n > b->n ? 1 : 0);
+}
+
+void oracle_indexer_topk(const float *scores, const int32_t *seg, int B, int S, int N, int K,
+                         int ratio, const int64_t *rows, int64_t nrows, int32_t *out_idx,
+                         float *out_val) {
+    if (!rows) nrows = (int64_t)B * S;
+    #pragma omp parallel
+    {
+        oracle_cand *c = (oracle_cand *)malloc(sizeof(oracle_cand) * (size_t)(N > 0 ? N : 1));
+        #pragma omp for schedule(dynamic, 8)
+        for (int64_t r = 0; r < nrows; ++r) {
+            int64_t row = row_of(rows, r);
+            int64_t b = row / S, t = row % S;
+            const float *sc = scores + row * (int64_t)N;
+            int m = 0;
+            for (int n = 0; n < N; ++n) {
+                int64_t last = (int64_t)ratio * n + ratio - 1;
+                if (last > t) continue;                       /* not complete at t (causal) */
+                int same = 1;
+                if (seg)
+                    for (int64_t j = (int64_t)ratio * n; j <= last; ++j)
+                        if (seg[b * S + j] != seg[b * S + t]) same = 0;
+                if (!same) continue;                          /* another document's block */
+                c[m].s = sc[n];
+                c[m].n = n;
+                ++m;
+            }
+            qsort(c, (size_t)m, sizeof(oracle_cand), cand_rank_cmp);
+            int kept = m < K ? m : K;
+            qsort(c, (size_t)kept, sizeof(oracle_cand), cand_index_cmp);
+            for (int k = 0; k < K; ++k) {
+                out_idx[r * (int64_t)K + k] = k < kept ? c[k].n : -1;
+                out_val[r * (int64_t)K + k] = k < kept ? c[k].s : -INFINITY;
+            }
+        }
+        free(c);
+    }
+}
+
+/* Gradient of the selection's values with respect to the block scores: the adjoint of the
+ * gather values[k] = scores[idx[k]] (valid slots, 0 <= idx < N).  Each block receives the
+ * gradients of the slots that hold it, added in slot order; every other entry is 0.
+ * out: [nrows, N] */
+void oracle_indexer_topk_bwd(const float *dval, const int32_t *idx, int B, int S, int N, int K,
+                             const int64_t *rows, int64_t nrows, double *out) {
+    if (!rows) nrows = (int64_t)B * S;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t row = row_of(rows, r);
+        double *o = out + r * (int64_t)N;
+        for (int n = 0; n < N; ++n) o[n] = 0.0;
+        for (int k = 0; k < K; ++k) {
+            int32_t n = idx[row * (int64_t)K + k];
+            if (n >= 0 && n < N) o[n] += (double)dval[row * (int64_t)K + k];
+        }
+    }
+}

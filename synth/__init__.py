@@ -131,6 +131,24 @@ def topk_slots(cfg: Config, rng: np.random.Generator, shuffle_pad: bool = False)
     return out
 
 
+def duplicate_slots(idx: np.ndarray, N: int, seed: int) -> np.ndarray:
+    """Copy of idx [B,S,K] in which, for about 70% of the rows with two or more valid slots,
+    one valid slot repeats another valid slot of the same row, and a row with a single valid
+    slot holds that block twice (the neighbouring slot is overwritten)."""
+    rng = np.random.default_rng(seed)
+    d = np.array(idx, copy=True)
+    B, S, K = d.shape
+    for b in range(B):
+        for t in range(S):
+            v = np.flatnonzero((d[b, t] >= 0) & (d[b, t] < N))
+            if len(v) >= 2 and rng.random() < 0.7:
+                src, dst = rng.choice(v, size=2, replace=False)
+                d[b, t, dst] = d[b, t, src]
+            elif len(v) == 1 and K > 1:
+                d[b, t, (v[0] + 1) % K] = d[b, t, v[0]]
+    return d
+
+
 def make_inputs(cfg: Config | str, shuffle_pad: bool = False) -> dict:
     """Draw every input of one workload.  Returns host tensors:
 

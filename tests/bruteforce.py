@@ -46,8 +46,10 @@ def selected_mask(idx_b: np.ndarray, N: int) -> np.ndarray:
     return m
 
 
-def target(q, pool, idx, kwin=None, sink=None, seg=None, W=0, scale=1.0, floor=0.0):
-    q, pool, kwin, sink = _np64(q), _np64(pool), _np64(kwin), _np64(sink)
+def target(q, pool, idx, kwin=None, sink=None, seg=None, W=0, scale=1.0, floor=0.0, extra=None):
+    """extra: optional [B,S,H] natural-log logits, one more column of each head's list
+    (a given non-compressed log-mass)."""
+    q, pool, kwin, sink, extra = _np64(q), _np64(pool), _np64(kwin), _np64(sink), _np64(extra)
     idx = np.asarray(idx)
     B, S, H, D = q.shape
     N = pool.shape[1]
@@ -67,6 +69,8 @@ def target(q, pool, idx, kwin=None, sink=None, seg=None, W=0, scale=1.0, floor=0
                 cols.append(np.where(wm, Lw, -np.inf))
             if sink is not None:
                 cols.append(np.full((S, 1), sink[h]))
+            if extra is not None:
+                cols.append(extra[b, :, h][:, None])
             full = logsumexp(np.concatenate(cols, axis=1), axis=1)      # [S]
             with np.errstate(invalid="ignore"):
                 P = np.where(sel, np.exp(Lp - full[:, None]), 0.0)

@@ -71,6 +71,76 @@ def test_window_lse_matches_dense_bruteforce(cfg):
         np.testing.assert_allclose(nc, ref.reshape(nc.shape), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("cfg", TINY_CASES[:4], ids=lambda c: c.name)
+def test_target_given_finite_nc_lse_matches_bruteforce_extra_column(cfg):
+    """The oracle's nc_lse input mode with finite values (natural log, indexed by the
+    compact output row): each head's list is [nc_lse] ++ [compressed logits].  Pinned
+    against the dense brute force with one extra column per (token, head), for all rows
+    and for a scattered subset of rows (whose nc_lse array holds only those rows)."""
+    x, c = _inputs(cfg)
+    rng = np.random.default_rng(cfg.cid)
+    nc = rng.normal(0.5, 2.0, size=(c.B, c.S, c.H))               # arbitrary log-masses
+    Tb = bf.target(x["q"], x["pool"], x["idx"], scale=c.scale, extra=nc).reshape(c.B * c.S, c.K)
+    T = oracle.target(x["q"], x["pool"], x["idx"], nc_lse=nc.reshape(-1, c.H), scale=c.scale)
+    np.testing.assert_allclose(T, Tb, rtol=0, atol=1e-12)
+    rows = np.sort(rng.choice(c.B * c.S, size=c.B * c.S // 3, replace=False))
+    Tr = oracle.target(x["q"], x["pool"], x["idx"], nc_lse=nc.reshape(-1, c.H)[rows], scale=c.scale, rows=rows)
+    np.testing.assert_allclose(Tr, Tb[rows], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("cfg", TINY_CASES[:4], ids=lambda c: c.name)
+def test_target_given_window_lse_equals_joint_list(cfg):
+    """Feeding window_lse's output back as nc_lse gives the joint-list target (window keys,
+    sink and compressed logits in one list), for all rows and a scattered subset."""
+    x, c = _inputs(cfg)
+    T = oracle.target(x["q"], x["pool"], x["idx"], x["kwin"], x["sink"], x["seg"], W=c.W, scale=c.scale)
+    nc = oracle.window_lse(x["q"], x["kwin"], x["sink"], x["seg"], c.W, c.scale)
+    Tn = oracle.target(x["q"], x["pool"], x["idx"], nc_lse=nc, scale=c.scale)
+    np.testing.assert_allclose(Tn, T, rtol=0, atol=1e-12)
+    rows = np.arange(c.B * c.S)[(np.arange(c.B * c.S) * 7919) % 5 < 2]
+    ncr = oracle.window_lse(x["q"], x["kwin"], x["sink"], x["seg"], c.W, c.scale, rows=rows)
+    Tr = oracle.target(x["q"], x["pool"], x["idx"], nc_lse=ncr, scale=c.scale, rows=rows)
+    np.testing.assert_allclose(Tr, T[rows], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("cfg", TINY_CASES[:4], ids=lambda c: c.name)
+def test_duplicate_slots_are_separate_softmax_entries(cfg):
+    """Reading: a block selected twice is two entries of the softmax.  The pin counts the
+    entries directly: every repeated occurrence is redirected to a fresh copy of the same
+    pool row (distinct rows, identical values), which the dense brute force can take."""
+    x, c = _inputs(cfg)
+    idx = synth.duplicate_slots(x["idx"].numpy(), c.N, cfg.cid)
+    assert (idx != x["idx"].numpy()).any()
+    pool = x["pool"].double().numpy()
+    extra_rows = []
+    idx_x = idx.copy()
+    for b in range(c.B):
+        for t in range(c.S):
+            seen = set()
+            for k in range(c.K):
+                n = idx[b, t, k]
+                if 0 <= n < c.N:
+                    if n in seen:
+                        idx_x[b, t, k] = c.N + len(extra_rows)
+                        extra_rows.append((b, n))
+                    seen.add(n)
+    Nx = c.N + len(extra_rows)
+    pool_x = np.zeros((c.B, Nx, c.D))
+    pool_x[:, : c.N] = pool
+    for i, (b, n) in enumerate(extra_rows):   # a copy row is selected only in its own batch
+        pool_x[b, c.N + i] = pool[b, n]
+    T = oracle.target(x["q"], x["pool"], idx, x["kwin"], x["sink"], x["seg"], W=c.W, scale=c.scale)
+    Tb = bf.target(x["q"], pool_x, idx_x, x["kwin"], x["sink"], x["seg"], W=c.W, scale=c.scale)
+    np.testing.assert_allclose(T, Tb.reshape(T.shape), rtol=0, atol=1e-12)
+    # the two occurrences of a block carry equal target values
+    Tr = T.reshape(c.B, c.S, c.K)
+    for b in range(c.B):
+        for t in range(c.S):
+            for n in set(idx[b, t][(idx[b, t] >= 0) & (idx[b, t] < c.N)].tolist()):
+                vals = Tr[b, t][idx[b, t] == n]
+                assert np.ptp(vals) == 0.0
+
+
 # ------------------------------------------------------------------ target closed forms
 def _softmax_valid(c, valid):
     c = torch.as_tensor(c, dtype=torch.float64)

@@ -155,8 +155,9 @@ int distill_target_fused(const void *q, const void *kwin, const float *sink, con
  *   workspace: device scratch of distill_kl_workspace_bytes(B,S,K) bytes, 16-byte
  *   aligned, owned by the caller; its contents need no initialisation and are
  *   overwritten.  Calls that share a workspace must be ordered (same stream).
- * Limits: K <= 4096; B * S <= 2^26 - 8 (one 512-lane workgroup per 8 rows, and a dispatch
- * counts at most 2^32 - 1 work-items).
+ * Limits: K <= 4096; B * S <= 2^24 (stats[1] is a float32 count, exact up to 2^24; larger
+ * requests return SD_ERR_UNSUPPORTED).  Target values may be subnormal: log T is taken exactly
+ * for every positive float32.
  */
 size_t distill_kl_workspace_bytes(int B, int S, int K);
 int distill_kl_fwd_bwd(const float *target, const float *logits, const int32_t *idx,

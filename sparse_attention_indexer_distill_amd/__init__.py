@@ -16,6 +16,7 @@ indexer distillation loss" and MaxText PR "Add Indexer Loss [Deepseek v4]"):
 from __future__ import annotations
 
 import ctypes
+import functools
 import math
 import os
 from typing import Optional, Tuple
@@ -138,6 +139,23 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
+def _on_stream(fn):
+    """Run a wrapper with ``stream`` (when given) as torch's current stream, so that every
+    temporary it makes (contiguous copies, dtype casts, slot remaps, default outputs and
+    workspaces) is allocated and written on the stream the kernels run on.  The caching
+    allocator then reuses those blocks only in that stream's order, after the kernels that
+    read them.  Inputs produced on another stream are the caller's to order, as for any
+    torch op run under a stream context."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, stream=None, **kw)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+    return wrapper
+
+
+@_on_stream
 def window_lse(q: torch.Tensor, kwin: torch.Tensor, sink: Optional[torch.Tensor] = None,
                seg: Optional[torch.Tensor] = None, *, W: int, scale: Optional[float] = None,
                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
@@ -168,6 +186,7 @@ def window_lse(q: torch.Tensor, kwin: torch.Tensor, sink: Optional[torch.Tensor]
     return out
 
 
+@_on_stream
 def distill_target(q: torch.Tensor, pool: torch.Tensor, idx: torch.Tensor,
                    nc_lse: Optional[torch.Tensor] = None, *, scale: Optional[float] = None,
                    l1_floor: float = 0.0, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
@@ -200,6 +219,7 @@ def distill_target(q: torch.Tensor, pool: torch.Tensor, idx: torch.Tensor,
     return out
 
 
+@_on_stream
 def distill_target_fused(q: torch.Tensor, kwin: torch.Tensor, pool: torch.Tensor, idx: torch.Tensor,
                          sink: Optional[torch.Tensor] = None, seg: Optional[torch.Tensor] = None, *, W: int,
                          scale: Optional[float] = None, l1_floor: float = 0.0, want_nc: bool = False,
@@ -250,6 +270,7 @@ def distill_kl_workspace_bytes(B: int, S: int, K: int) -> int:
     return int(load_library().distill_kl_workspace_bytes(B, S, K))
 
 
+@_on_stream
 def distill_kl_fwd_bwd(target: torch.Tensor, logits: torch.Tensor, idx: torch.Tensor, N: int, *,
                        grad_scale: float = 1.0, want_grad: bool = True,
                        kl_rows: Optional[torch.Tensor] = None, dlogits: Optional[torch.Tensor] = None,
@@ -285,6 +306,7 @@ def distill_kl_fwd_bwd(target: torch.Tensor, logits: torch.Tensor, idx: torch.Te
     return kl_rows, dlogits, stats
 
 
+@_on_stream
 def csa_distill_layer(q, kwin, pool, idx, logits, sink=None, seg=None, *, W: int,
                       scale: Optional[float] = None, grad_scale: float = 1.0, want_grad: bool = True,
                       fused: bool = False, bufs: Optional[dict] = None, stream=None):

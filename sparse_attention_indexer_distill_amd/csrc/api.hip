@@ -147,8 +147,10 @@ int distill_kl_fwd_bwd(const float *target, const float *logits, const int32_t *
     if (B <= 0 || S <= 0 || K <= 0 || N <= 0)
         return fail(SD_ERR_BAD_SHAPE, "distill_kl_fwd_bwd: sizes must be positive (B=%d S=%d K=%d N=%d)", B, S, K, N);
     if (K > sd::kMaxKlK) return fail(SD_ERR_UNSUPPORTED, "distill_kl_fwd_bwd: K=%d exceeds %d", K, sd::kMaxKlK);
-    int st = check_grid("distill_kl_fwd_bwd", ((int64_t)B * S + 7) / 8, 512, "B*S must be at most 2^26 - 8");
-    if (st != SD_OK) return st;
+    // stats[1] counts rows in float32, which is exact up to 2^24
+    if ((int64_t)B * S > ((int64_t)1 << 24))
+        return fail(SD_ERR_UNSUPPORTED, "distill_kl_fwd_bwd: B*S=%lld exceeds 2^24 rows (the float32 row count "
+                    "in stats[1] is exact only up to 2^24)", (long long)B * S);
     if (!isfinite(grad_scale)) return fail(SD_ERR_BAD_SHAPE, "distill_kl_fwd_bwd: grad_scale must be finite");
     const size_t need = sd::kl_workspace_bytes(B, S, K);
     if (workspace_bytes < need)

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kKlRowsPerBlock * 64) void distill_kl_kernel(
             float kl2 = 0.f;  // KL in log2 units: T (log2 T - log2 Q) with log2 Q = y - lse2
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                kl2 += (vv[e] && tv[e] > 0.f) ? tv[e] * (fast_log2(tv[e]) - (zv[e] - lse2)) : 0.f;
+                kl2 += (vv[e] && tv[e] > 0.f) ? tv[e] * (log2_full(tv[e]) - (zv[e] - lse2)) : 0.f;
                 zv[e] = grad_scale * (sumT * (qv[e] * rse) - tv[e]);  // gradient (0 at invalid slots)
             }
             const float kl = wave_sum(kl2) * kLn2;

@@ -22,6 +22,7 @@
 // from them without a second exchange, and the head sum of p[h,k] = exp(c[h,k] - full_h)
 // is a 16-lane DPP transpose-reduction.  Nothing but the target row is written.
 #include <float.h>
+#include <math.h>
 
 #include "sd_device.hpp"
 #include "sd_internal.hpp"
@@ -410,19 +411,26 @@ __device__ __forceinline__ void tr_step(float (&v)[16], bool hi) {
 //   full_h = log2(sum_k 2^c_hk + 2^(nc_h log2 e))  (lane (g, x) reduces head 16g+x over waves)
 //   row total sum_k m_k = sum_h 2^(clse_h - full_h), clse_h = log2 sum_k 2^c_hk, which needs
 //   no further exchange between waves
-//   T_k = sum_h exp2(c_hk - mloc_h) * 2^(mloc_h - full_h) / max(total, floor)
-// The head sum is a 16-lane transpose-reduction: afterwards lane (g, x) holds T of row
-// 4g + (x%4) of tile x/4 and stores it at its slot.  nc: the natural-log nc_lse of head
-// 16*min(g, HT-1)+x (ignored when has_nc is false).
+//   T_k = sum_h exp2(c_hk - mloc_h) * 2^(mloc_h - full_h - lmax) / max(total', 2^(floor - lmax))
+//   with lmax = max_h (clse_h - full_h) and total' = sum_h 2^(clse_h - full_h - lmax) in [1, H]
+// Shifting every head's log-share by the largest one keeps the row total and the weights in
+// range however small the row's mass is (below float32 tiny the floor term wins and still
+// scales exactly), and the shifted exponents of heads near the largest are exact
+// differences of nearby floats, so a row whose target is a single slot still sums to 1
+// within an ulp even when the log-masses are large (a sink far above the logits).  The
+// head sum is a 16-lane
+// transpose-reduction: afterwards lane (g, x) holds T of row 4g + (x%4) of tile x/4 and
+// stores it at its slot.  nc: the natural-log nc_lse of head 16*min(g, HT-1)+x (ignored when
+// has_nc is false).
 template <int HT, int KT, int NW>
 __device__ __forceinline__ void epi_target(const f32x4 (&acc)[KT][HT], const float (&mloc)[HT], int my, int nv, int w,
-                                           int lane, int H, bool has_nc, float nc, float l1_floor, const float *red_m,
+                                           int lane, int H, bool has_nc, float nc, float floor_log2, const float *red_m,
                                            const float *red_s, const int32_t *cslot, float *Tr) {
     static_assert(KT <= 4, "at most 16 rows per lane");
     const int x = lane & 15, g = lane >> 4;
     const int gg = g < HT ? g : HT - 1;
     const bool head_ok = g < HT && gg * 16 + x < H;
-    float full, share;
+    float full, lshare;
     {
         float M = -INFINITY;
 #pragma unroll 4
@@ -433,16 +441,18 @@ __device__ __forceinline__ void epi_target(const f32x4 (&acc)[KT][HT], const flo
             ssum = fmaf(red_s[(i * 16 + x) * HT + gg], fast_exp2(red_m[(i * 16 + x) * HT + gg] - M), ssum);
         const float clse = M + fast_log2(ssum);
         full = (has_nc && head_ok) ? logaddexp2(clse, nc * kLog2e) : clse;
-        share = head_ok ? fast_exp2(clse - full) : 0.f;  // this head's share of the joint mass
+        lshare = head_ok ? clse - full : -INFINITY;  // log2 of this head's share of the joint mass
     }
-    const float tot = cols4_sum(row16_sum(share));
-    const float rden = 1.f / fmaxf(tot, l1_floor);
+    const float lmax = cols4_max(row16_butterfly<true>(lshare));  // finite: some head is valid
+    const float tot = cols4_sum(row16_sum(head_ok ? fast_exp2(lshare - lmax) : 0.f));
+    // 2^(floor - lmax) overflows to +inf only when the true target underflows to 0 anyway
+    const float rden = 1.f / fmaxf(tot, fast_exp2(floor_log2 - lmax));
     float fr[4];
     rows_bcast(full, fr);  // fr[ht]: full of head 16ht + x
     float wgt[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
-        wgt[ht] = (ht * 16 + x < H && mloc[ht] != -INFINITY) ? fast_exp2(mloc[ht] - fr[ht]) * rden : 0.f;
+        wgt[ht] = (ht * 16 + x < H && mloc[ht] != -INFINITY) ? fast_exp2((mloc[ht] - fr[ht]) - lmax) * rden : 0.f;
     float v[16];
 #pragma unroll
     for (int l = 0; l < 4; ++l)
@@ -475,7 +485,7 @@ struct TargetArgs {
     float *nc_out;        // [B,S,H] or NULL: the window+sink LSE as a by-product
     int W;
     int B, S, H, D, N, K;
-    float scale_log2, l1_floor;
+    float scale_log2, floor_log2;  // log2 of the L1 floor
     float *target;
 };
 
@@ -683,8 +693,8 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
     epi_stats<HT, KT, NW>(acc, mloc, my, nv, w, lane, a.scale_log2, red_m, red_s);
     __syncthreads();
     if constexpr (FUSED) window_done();
-    epi_target<HT, KT, NW>(acc, mloc, my, nv, w, lane, H, FUSED || a.nc_lse != nullptr, nc, a.l1_floor, red_m, red_s,
-                           cslot, Tr);
+    epi_target<HT, KT, NW>(acc, mloc, my, nv, w, lane, H, FUSED || a.nc_lse != nullptr, nc, a.floor_log2, red_m,
+                           red_s, cslot, Tr);
 }
 
 template <int DT, int HT, int KT, int NW, bool FUSED>
@@ -692,11 +702,10 @@ hipError_t launch3(const TargetArgs &a, hipStream_t stream) {
     const size_t red = (size_t)NW * 16 * HT * 4;
     const size_t qbytes = DT == 0 ? (size_t)2048 * HT * (((a.D >> 5) + 1) >> 1) : (size_t)16 * HT * (a.D * 4 + 16);
     const size_t lds = qbytes + (size_t)8 * a.K + 2 * red + (size_t)2 * NW * 4 + (FUSED ? 2 * red : 0);
-    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    if (lds > (size_t)kLdsBytes) return hipErrorInvalidValue;
     auto kfn = &distill_target_kernel<DT, HT, KT, NW, FUSED>;
-    if (lds > 65536) {  // opt in to more than 64 KiB of LDS per workgroup (gfx950 has 160 KiB per CU)
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kfn),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (lds > 65536) {  // more than the default 64 KiB of LDS per workgroup
+        const hipError_t e = allow_full_lds<&distill_target_kernel<DT, HT, KT, NW, FUSED>>();
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kfn, dim3((unsigned)((int64_t)a.B * a.S)), dim3(NW * 64), lds, stream, a);
@@ -728,7 +737,7 @@ hipError_t launch1(const TargetArgs &a, hipStream_t stream) {
 template <bool FUSED>
 hipError_t launch0(TargetArgs a, float scale, float l1_floor, int dtype, hipStream_t stream) {
     a.scale_log2 = scale * kLog2e;
-    a.l1_floor = l1_floor > 0.f ? l1_floor : FLT_MIN;
+    a.floor_log2 = l1_floor > 0.f ? (float)log2((double)l1_floor) : -126.f;  // FLT_MIN = 2^-126
     if (dtype == 0) return launch1<0, FUSED>(a, stream);
     return launch1<1, FUSED>(a, stream);
 }

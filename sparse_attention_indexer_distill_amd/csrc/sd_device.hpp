@@ -235,6 +235,14 @@ __device__ __forceinline__ float wave_sum(float v) { return cols4_sum(row16_butt
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// log2 of a positive finite value, exact for subnormal inputs too: v_log_f32 takes no
+// subnormal operands, so values below 2^-126 are scaled by 2^32 first (an exact power-of-two
+// scaling) and 32 is subtracted from the result.
+__device__ __forceinline__ float log2_full(float x) {
+    const bool sub = x < 1.17549435e-38f;
+    return fast_log2(sub ? x * 4294967296.0f : x) - (sub ? 32.0f : 0.0f);
+}
+
 // log2(2^a + 2^b), with -inf handled.
 __device__ __forceinline__ float logaddexp2(float a, float b) {
     float m = fmaxf(a, b);

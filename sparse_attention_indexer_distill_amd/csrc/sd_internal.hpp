@@ -7,7 +7,29 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace sd {
+
+// LDS per CU on gfx950.
+constexpr int kLdsBytes = 160 * 1024;
+
+// Opts kernel KFN in to the whole 160 KiB of LDS as dynamic shared memory (the default cap
+// is 64 KiB).  The attribute is set once per (kernel, device) -- not on every launch -- and
+// remembered in a per-kernel bit mask of devices (devices past 63 set it on every call).
+template <auto KFN>
+hipError_t allow_full_lds() {
+    static std::atomic<uint64_t> done{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(KFN), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kLdsBytes);
+    if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 // Largest head count / head dim / top-k the kernels are instantiated for.
 constexpr int kMaxHeads = 64;

@@ -322,9 +322,9 @@ hipError_t launch_mfma(const void *q, const void *kwin, const float *sink, const
     const int nballoc = std::max(win_tiles(W + kTokMfma - 1), NBT + 1);
     const size_t lds = (size_t)2 * nballoc * 16 * 128 + (size_t)2 * kTokMfma * HG * 16 * 128 + (size_t)nballoc * 16 * 4;
     auto kfn = &window_lse_mfma_kernel<NBT>;
-    if (lds > 65536) {  // opt in to more than 64 KiB of LDS per workgroup (gfx950 has 160 KiB per CU)
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kfn),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (lds > (size_t)kLdsBytes) return hipErrorInvalidValue;
+    if (lds > 65536) {  // more than the default 64 KiB of LDS per workgroup
+        const hipError_t e = allow_full_lds<&window_lse_mfma_kernel<NBT>>();
         if (e != hipSuccess) return e;
     }
     dim3 grid((S + kTokMfma - 1) / kTokMfma, B);

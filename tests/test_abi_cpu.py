@@ -157,10 +157,12 @@ def test_distill_kl_rejections(lib):
     assert _kl(lib, wsb=7) == sd.SD_ERR_BAD_SHAPE  # one 8-row block needs 8 bytes
     assert b"workspace" in lib.sd_last_error()
     assert _kl(lib, K=4097) == sd.SD_ERR_UNSUPPORTED
-    # 512 lanes per 8 rows: B*S at most 2^26 - 8
-    assert _kl(lib, B=1, S=(1 << 26) - 7) == sd.SD_ERR_UNSUPPORTED
-    assert _kl(lib, B=2, S=1 << 25) == sd.SD_ERR_UNSUPPORTED
-    assert b"2^26 - 8" in lib.sd_last_error()
+    # stats[1] is a float32 row count, exact up to 2^24: B*S at most 2^24
+    assert _kl(lib, B=1, S=(1 << 24) + 1) == sd.SD_ERR_UNSUPPORTED
+    assert b"2^24" in lib.sd_last_error()
+    assert _kl(lib, B=2, S=(1 << 23) + 1) == sd.SD_ERR_UNSUPPORTED
+    assert _kl(lib, B=4, S=1 << 22, wsb=7) == sd.SD_ERR_BAD_SHAPE        # 2^24 rows exactly: admitted
+    assert _kl(lib, B=1 << 10, S=1 << 14, wsb=7) == sd.SD_ERR_BAD_SHAPE
     assert _kl(lib, ws=ctypes.c_void_p(0x1004)) == sd.SD_ERR_BAD_SHAPE   # not 16-byte aligned
 
 

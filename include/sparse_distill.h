@@ -165,6 +165,23 @@ int distill_kl_fwd_bwd(const float *target, const float *logits, const int32_t *
                        float *dlogits, float *stats, void *workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/*
+ * distill_kl_fwd_bwd_noalloc -- distill_kl_fwd_bwd without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  Same arguments, results and limits as distill_kl_fwd_bwd
+ * minus the workspace; the call allocates nothing.
+ *
+ * The per-block partial sums live in a fixed 2 MiB array of the library's device memory,
+ * one per GPU, held until the process ends (its address is resolved on the first call on
+ * each device).  Hence B * S <= 2^21 (larger requests return SD_ERR_UNSUPPORTED: use
+ * distill_kl_fwd_bwd with a workspace).  Every call on a GPU uses that GPU's array and
+ * overwrites what it reads, so calls ordered on one stream are fine, but calls that overlap
+ * in time on one GPU (unordered streams, or other host threads) race on it.
+ */
+int distill_kl_fwd_bwd_noalloc(const float *target, const float *logits, const int32_t *idx,
+                               int B, int S, int K, int N, float grad_scale, float *kl_rows,
+                               float *dlogits, float *stats, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *sd_status_string(int status);
 /* Detail of the last non-OK status returned on the calling thread ("" if none). */

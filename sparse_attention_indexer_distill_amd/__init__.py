@@ -24,7 +24,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["window_lse", "distill_target", "distill_target_fused", "distill_kl_fwd_bwd", "distill_kl_workspace_bytes",
-           "csa_distill_layer", "library_path", "load_library", "SD_BF16", "SD_F32"]
+           "distill_kl_fwd_bwd_noalloc", "csa_distill_layer", "library_path", "load_library", "SD_BF16", "SD_F32"]
 
 SD_OK, SD_ERR_NULL_ARG, SD_ERR_BAD_SHAPE, SD_ERR_UNSUPPORTED, SD_ERR_DTYPE, SD_ERR_HIP = range(6)
 SD_BF16, SD_F32 = 0, 1
@@ -62,6 +62,8 @@ def load_library():
     lib.distill_kl_workspace_bytes.restype = ctypes.c_size_t
     lib.distill_kl_fwd_bwd.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.distill_kl_fwd_bwd.restype = _i
+    lib.distill_kl_fwd_bwd_noalloc.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp]
+    lib.distill_kl_fwd_bwd_noalloc.restype = _i
     lib.sd_status_string.argtypes = [_i]
     lib.sd_status_string.restype = ctypes.c_char_p
     lib.sd_last_error.argtypes = []
@@ -303,6 +305,40 @@ def distill_kl_fwd_bwd(target: torch.Tensor, logits: torch.Tensor, idx: torch.Te
                                 _ptr(kl_rows), _ptr(dlogits), _ptr(stats), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(dev, stream))
     _check(st, "distill_kl_fwd_bwd")
+    return kl_rows, dlogits, stats
+
+
+@_on_stream
+def distill_kl_fwd_bwd_noalloc(target: torch.Tensor, logits: torch.Tensor, idx: torch.Tensor, N: int, *,
+                               grad_scale: float = 1.0, want_grad: bool = True,
+                               kl_rows: Optional[torch.Tensor] = None, dlogits: Optional[torch.Tensor] = None,
+                               stats: Optional[torch.Tensor] = None,
+                               stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor], torch.Tensor]:
+    """distill_kl_fwd_bwd without a workspace: the library keeps its partial sums in a fixed
+    per-GPU array and the C call allocates nothing (B*S <= 2^21; calls overlapping on one
+    GPU race).  Outputs not passed in are allocated here, by torch."""
+    lib = load_library()
+    dev = target.device
+    target = _dev(target, "target", dev)
+    logits = _dev(logits, "logits", dev)
+    if target.dim() != 3 or logits.shape != target.shape or idx.shape != target.shape:
+        raise ValueError("target, logits and idx must share one [B,S,K] shape")
+    if target.dtype != torch.float32 or logits.dtype != torch.float32:
+        raise ValueError("target and logits must be float32")
+    idx = _slots(idx, int(N), dev)
+    B, S, K = target.shape
+    kl_rows = torch.empty((B, S), dtype=torch.float32, device=dev) if kl_rows is None else \
+        _out(kl_rows, "kl_rows", (B, S), dev)
+    if not want_grad:
+        dlogits = None
+    elif dlogits is None:
+        dlogits = torch.empty((B, S, K), dtype=torch.float32, device=dev)
+    else:
+        _out(dlogits, "dlogits", (B, S, K), dev)
+    stats = torch.empty(2, dtype=torch.float32, device=dev) if stats is None else _out(stats, "stats", (2,), dev)
+    st = lib.distill_kl_fwd_bwd_noalloc(_ptr(target), _ptr(logits), _ptr(idx), B, S, K, int(N), float(grad_scale),
+                                        _ptr(kl_rows), _ptr(dlogits), _ptr(stats), _stream(dev, stream))
+    _check(st, "distill_kl_fwd_bwd_noalloc")
     return kl_rows, dlogits, stats
 
 

@@ -162,4 +162,24 @@ int distill_kl_fwd_bwd(const float *target, const float *logits, const int32_t *
                       "distill_kl_fwd_bwd launch");
 }
 
+int distill_kl_fwd_bwd_noalloc(const float *target, const float *logits, const int32_t *idx, int B, int S, int K,
+                               int N, float grad_scale, float *kl_rows, float *dlogits, float *stats,
+                               hipStream_t stream) {
+    if (!target || !logits || !idx || !kl_rows || !stats)
+        return fail(SD_ERR_NULL_ARG, "distill_kl_fwd_bwd_noalloc: target, logits, idx, kl_rows and stats are required");
+    if (B <= 0 || S <= 0 || K <= 0 || N <= 0)
+        return fail(SD_ERR_BAD_SHAPE, "distill_kl_fwd_bwd_noalloc: sizes must be positive (B=%d S=%d K=%d N=%d)", B, S,
+                    K, N);
+    if (K > sd::kMaxKlK)
+        return fail(SD_ERR_UNSUPPORTED, "distill_kl_fwd_bwd_noalloc: K=%d exceeds %d", K, sd::kMaxKlK);
+    if ((int64_t)B * S > sd::kNoAllocMaxRows)
+        return fail(SD_ERR_UNSUPPORTED, "distill_kl_fwd_bwd_noalloc: B*S=%lld exceeds the %lld rows its fixed scratch "
+                    "array holds; use distill_kl_fwd_bwd with a workspace", (long long)B * S,
+                    (long long)sd::kNoAllocMaxRows);
+    if (!isfinite(grad_scale)) return fail(SD_ERR_BAD_SHAPE, "distill_kl_fwd_bwd_noalloc: grad_scale must be finite");
+    return hip_status(sd::launch_distill_kl_noalloc(target, logits, idx, B, S, K, N, grad_scale, kl_rows, dlogits,
+                                                    stats, stream),
+                      "distill_kl_fwd_bwd_noalloc launch");
+}
+
 }  // extern "C"

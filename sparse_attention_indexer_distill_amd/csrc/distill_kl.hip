@@ -14,6 +14,9 @@
 // reproducible.  (A last-block-reduces variant in the same launch needs device-scope
 // fences per block, which write back and invalidate L2 and cost far more than the
 // second launch.)
+#include <atomic>
+#include <mutex>
+
 #include "sd_device.hpp"
 #include "sd_internal.hpp"
 
@@ -195,6 +198,45 @@ hipError_t launch_e(const float *target, const float *logits, const int32_t *idx
 
 }  // namespace
 
+// Per-block partials of the allocation-free entry point: one fixed array per GPU, in the
+// library's device memory for the life of the process.  Host code never passes the array's
+// name to a kernel (in host code it names a host-side stand-in); it resolves the device
+// address with hipGetSymbolAddress once per device and passes that.
+__device__ __align__(256) float scratch[kNoAllocMaxRows / 8 * 2];
+
+namespace {
+
+static_assert(kKlRowsPerBlock == 8, "scratch holds one (sum, count) pair per 8-row block");
+constexpr int kMaxDevices = 64;
+std::atomic<float *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (resolved on the first call per device,
+// with that device current).
+hipError_t scratch_for_current_device(float **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    float *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            void *addr = nullptr;
+            e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (addr == nullptr) return hipErrorInvalidSymbol;
+            p = reinterpret_cast<float *>(addr);
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+}  // namespace
+
 size_t kl_workspace_bytes(int B, int S, int K) {
     (void)K;
     const int64_t rows = (int64_t)B * S;
@@ -224,6 +266,16 @@ hipError_t launch_distill_kl(const float *target, const float *logits, const int
     if (K <= 2048) return SD_K(1, 32);
     return SD_K(1, 64);
 #undef SD_K
+}
+
+hipError_t launch_distill_kl_noalloc(const float *target, const float *logits, const int32_t *idx, int B, int S,
+                                     int K, int N, float grad_scale, float *kl_rows, float *dlogits, float *stats,
+                                     hipStream_t stream) {
+    float *partials = nullptr;
+    const hipError_t e = scratch_for_current_device(&partials);
+    if (e != hipSuccess) return e;
+    // every partial the finalize reads is written by this call's first kernel: nothing to clear
+    return launch_distill_kl(target, logits, idx, B, S, K, N, grad_scale, kl_rows, dlogits, stats, partials, stream);
 }
 
 }  // namespace sd

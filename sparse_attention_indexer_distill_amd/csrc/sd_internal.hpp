@@ -52,6 +52,11 @@ hipError_t launch_distill_target_fused(const void *q, const void *kwin, const fl
                                        float *nc_out, hipStream_t stream);
 
 size_t kl_workspace_bytes(int B, int S, int K);
+// Rows the allocation-free KL entry point takes (its partials live in a fixed 2 MiB array).
+constexpr int64_t kNoAllocMaxRows = (int64_t)1 << 21;
+hipError_t launch_distill_kl_noalloc(const float *target, const float *logits, const int32_t *idx, int B, int S,
+                                     int K, int N, float grad_scale, float *kl_rows, float *dlogits, float *stats,
+                                     hipStream_t stream);
 hipError_t launch_distill_kl(const float *target, const float *logits, const int32_t *idx, int B, int S,
                              int K, int N, float grad_scale, float *kl_rows, float *dlogits, float *stats,
                              void *workspace, hipStream_t stream);

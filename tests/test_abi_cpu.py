@@ -34,7 +34,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("window_lse", "distill_target", "distill_target_fused", "distill_kl_fwd_bwd",
-              "distill_kl_workspace_bytes", "sd_status_string", "sd_last_error"):
+              "distill_kl_workspace_bytes", "distill_kl_fwd_bwd_noalloc", "sd_status_string", "sd_last_error"):
         assert n in names, names
 
 
@@ -164,6 +164,20 @@ def test_distill_kl_rejections(lib):
     assert _kl(lib, B=4, S=1 << 22, wsb=7) == sd.SD_ERR_BAD_SHAPE        # 2^24 rows exactly: admitted
     assert _kl(lib, B=1 << 10, S=1 << 14, wsb=7) == sd.SD_ERR_BAD_SHAPE
     assert _kl(lib, ws=ctypes.c_void_p(0x1004)) == sd.SD_ERR_BAD_SHAPE   # not 16-byte aligned
+
+
+def test_noalloc_kl_rejections(lib):
+    def call(B=1, S=8, K=4, N=2, T=FAKE, st=FAKE, g=1.0):
+        return lib.distill_kl_fwd_bwd_noalloc(T, FAKE, FAKE, B, S, K, N, g, FAKE, FAKE, st, None)
+    assert call(T=None) == sd.SD_ERR_NULL_ARG
+    assert call(st=None) == sd.SD_ERR_NULL_ARG
+    assert call(N=0) == sd.SD_ERR_BAD_SHAPE
+    assert call(K=4097) == sd.SD_ERR_UNSUPPORTED
+    assert call(g=float("inf")) == sd.SD_ERR_BAD_SHAPE
+    # its fixed scratch array holds the partials of 2^21 rows
+    assert call(B=1, S=(1 << 21) + 1) == sd.SD_ERR_UNSUPPORTED
+    assert b"2097152 rows" in lib.sd_last_error()
+    assert call(B=2, S=(1 << 20) + 8) == sd.SD_ERR_UNSUPPORTED
 
 
 def test_binding_rejects_host_tensors():

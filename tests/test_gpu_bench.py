@@ -32,7 +32,8 @@ def test_bench_prints_one_complete_json_line(monkeypatch, capsys):
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
     # achieved = useful FLOP of one launch / its mean duration
     kt = k["distill_target_fused"]
-    assert abs(r["achieved"] - kt["algorithmic_flops"] / (kt["ms"] * 1e-3) / 1e12) <= 0.1
+    # (kt["ms"] is rounded to 4 decimals: up to ~3e-4 relative at 0.2 ms)
+    assert abs(r["achieved"] - kt["algorithmic_flops"] / (kt["ms"] * 1e-3) / 1e12) <= 1e-3 * r["achieved"] + 0.1
     # HBM counters, when the committed summary matches this kernel source, cover at least
     # the compulsory bytes
     assert r["traffic"] is None or r["traffic"] >= 0.95 * kt["algorithmic_bytes"]

@@ -166,6 +166,50 @@ int distill_kl_fwd_bwd(const float *target, const float *logits, const int32_t *
                        hipStream_t stream);
 
 /*
+ * indexer_topk -- the indexer's top-k block selection under the causal block mask and the
+ * segment (packing) mask: the step that produces idx and the student logits of the KL.
+ *
+ *   block n covers tokens ratio*n .. ratio*n + ratio - 1 of its batch row; it is VISIBLE to
+ *   token t iff n < N, ratio*n + ratio - 1 <= t (complete at t) and every one of its tokens
+ *   carries seg[b,t]'s id (seg NULL: one segment).
+ *   idx[b,t,:]    = the min(K, #visible) visible blocks with the largest scores[b,t,n], in
+ *                   ascending block order, then -1.  Equal scores prefer the smaller block
+ *                   index; a NaN score ranks below every number (-inf included).
+ *   values[b,t,k] = scores[b,t,idx[b,t,k]];  -inf at a -1 slot
+ *
+ * Defined by the MaxText PR "Add Indexer Loss [Deepseek v4]": the indexer keeps the top-k
+ * compressed blocks of each query, the teacher and the student share the causal block mask
+ * combined with the segment/packing mask (commit list: no probability mass on future
+ * blocks; for t = 4 block 0 is visible and block 1 is not, compress ratio 4), and the slots
+ * it cannot fill become -1 (review comment on jnp.where(invalid, -1, top_k_indices)).  The
+ * kept set is what distill_target and distill_kl_fwd_bwd use; its order within a row does
+ * not change their results, and ascending block order is the one written here.
+ *
+ *   scores [B,S,N] float32       the student's per-(token, block) scores
+ *   seg    [B,S]   int32 or NULL packed-segment ids
+ *   idx    [B,S,K] int32 out;  values [B,S,K] float32 out or NULL
+ * Limits: 1 <= N <= 4096; 1 <= K <= 4096; ratio >= 1; B * S < 2^26 (one 256-lane workgroup
+ * per four rows).
+ */
+int indexer_topk(const float *scores, const int32_t *seg, int B, int S, int N, int K, int ratio,
+                 int32_t *idx, float *values, hipStream_t stream);
+
+/*
+ * indexer_topk_bwd -- gradient of indexer_topk's values with respect to the scores: the
+ * adjoint of the gather values[b,t,k] = scores[b,t,idx[b,t,k]].
+ *
+ *   dscores[b,t,n] = sum of dvalues[b,t,k] over the slots k with idx[b,t,k] == n, added in
+ *                    slot order;  0 for every block no slot holds
+ * A slot is valid iff 0 <= idx < N (-1 and out-of-range slots carry no gradient).  Slots
+ * of one selection are distinct, so each kept block receives exactly its slot's gradient.
+ *
+ *   dvalues [B,S,K] float32;  idx [B,S,K] int32;  dscores [B,S,N] float32 out (all written)
+ * Limits: 1 <= N <= 4096; 1 <= K <= 4096; B * S < 2^26.
+ */
+int indexer_topk_bwd(const float *dvalues, const int32_t *idx, int B, int S, int N, int K,
+                     float *dscores, hipStream_t stream);
+
+/*
  * distill_kl_fwd_bwd_noalloc -- distill_kl_fwd_bwd without a workspace argument, for callers
  * that cannot allocate device memory: code under HIP graph capture, tight serving loops and
  * harnesses that forbid hipMalloc.  Same arguments, results and limits as distill_kl_fwd_bwd

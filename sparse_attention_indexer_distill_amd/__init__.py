@@ -24,7 +24,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["window_lse", "distill_target", "distill_target_fused", "distill_kl_fwd_bwd", "distill_kl_workspace_bytes",
-           "distill_kl_fwd_bwd_noalloc", "csa_distill_layer", "library_path", "load_library", "SD_BF16", "SD_F32"]
+           "distill_kl_fwd_bwd_noalloc", "indexer_topk", "indexer_topk_bwd", "csa_distill_layer", "library_path", "load_library", "SD_BF16", "SD_F32"]
 
 SD_OK, SD_ERR_NULL_ARG, SD_ERR_BAD_SHAPE, SD_ERR_UNSUPPORTED, SD_ERR_DTYPE, SD_ERR_HIP = range(6)
 SD_BF16, SD_F32 = 0, 1
@@ -64,6 +64,10 @@ def load_library():
     lib.distill_kl_fwd_bwd.restype = _i
     lib.distill_kl_fwd_bwd_noalloc.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp]
     lib.distill_kl_fwd_bwd_noalloc.restype = _i
+    lib.indexer_topk.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]
+    lib.indexer_topk.restype = _i
+    lib.indexer_topk_bwd.argtypes = [_vp, _vp, _i, _i, _i, _i, _vp, _vp]
+    lib.indexer_topk_bwd.restype = _i
     lib.sd_status_string.argtypes = [_i]
     lib.sd_status_string.restype = ctypes.c_char_p
     lib.sd_last_error.argtypes = []
@@ -340,6 +344,61 @@ def distill_kl_fwd_bwd_noalloc(target: torch.Tensor, logits: torch.Tensor, idx: 
                                         _ptr(kl_rows), _ptr(dlogits), _ptr(stats), _stream(dev, stream))
     _check(st, "distill_kl_fwd_bwd_noalloc")
     return kl_rows, dlogits, stats
+
+
+@_on_stream
+def indexer_topk(scores: torch.Tensor, seg: Optional[torch.Tensor] = None, *, K: int, ratio: int = 4,
+                 want_values: bool = True, out_idx: Optional[torch.Tensor] = None,
+                 out_values: Optional[torch.Tensor] = None, stream=None):
+    """The indexer's masked top-k: idx [B,S,K] int32 (visible blocks with the largest scores,
+    ascending block order, -1 after) and values [B,S,K] fp32 (their scores, -inf at -1), or
+    (idx, None) when want_values is False.  scores [B,S,N] fp32; seg [B,S] or None."""
+    lib = load_library()
+    dev = scores.device
+    scores = _dev(scores, "scores", dev)
+    if scores.dim() != 3 or scores.dtype != torch.float32:
+        raise ValueError("scores must be a float32 [B,S,N] tensor")
+    B, S, N = scores.shape
+    if seg is not None:
+        seg = _dev(seg.to(torch.int32), "seg", dev)
+        if seg.shape != (B, S):
+            raise ValueError(f"seg must be [{B},{S}]")
+    if out_idx is None:
+        out_idx = torch.empty((B, S, int(K)), dtype=torch.int32, device=dev)
+    elif (not out_idx.is_cuda or out_idx.device != dev or tuple(out_idx.shape) != (B, S, int(K))
+          or out_idx.dtype != torch.int32 or not out_idx.is_contiguous()):
+        raise ValueError(f"out_idx must be a contiguous int32 [{B},{S},{K}] tensor on {dev}")
+    if not want_values:
+        out_values = None
+    elif out_values is None:
+        out_values = torch.empty((B, S, int(K)), dtype=torch.float32, device=dev)
+    else:
+        _out(out_values, "out_values", (B, S, int(K)), dev)
+    st = lib.indexer_topk(_ptr(scores), _ptr(seg), B, S, N, int(K), int(ratio), _ptr(out_idx), _ptr(out_values),
+                          _stream(dev, stream))
+    _check(st, "indexer_topk")
+    return out_idx, out_values
+
+
+@_on_stream
+def indexer_topk_bwd(dvalues: torch.Tensor, idx: torch.Tensor, N: int, *, out: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """Gradient of indexer_topk's values w.r.t. the scores: dscores [B,S,N] fp32, each block
+    receiving the sum of its slots' dvalues (0 elsewhere)."""
+    lib = load_library()
+    dev = dvalues.device
+    dvalues = _dev(dvalues, "dvalues", dev)
+    if dvalues.dim() != 3 or dvalues.dtype != torch.float32 or idx.shape != dvalues.shape:
+        raise ValueError("dvalues must be float32 [B,S,K] and idx the same shape")
+    idx = _slots(idx, int(N), dev)
+    B, S, K = dvalues.shape
+    if out is None:
+        out = torch.empty((B, S, int(N)), dtype=torch.float32, device=dev)
+    else:
+        _out(out, "out", (B, S, int(N)), dev)
+    st = lib.indexer_topk_bwd(_ptr(dvalues), _ptr(idx), B, S, int(N), K, _ptr(out), _stream(dev, stream))
+    _check(st, "indexer_topk_bwd")
+    return out
 
 
 @_on_stream

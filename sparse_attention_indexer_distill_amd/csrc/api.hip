@@ -162,6 +162,36 @@ int distill_kl_fwd_bwd(const float *target, const float *logits, const int32_t *
                       "distill_kl_fwd_bwd launch");
 }
 
+int indexer_topk(const float *scores, const int32_t *seg, int B, int S, int N, int K, int ratio, int32_t *idx,
+                 float *values, hipStream_t stream) {
+    if (!scores || !idx) return fail(SD_ERR_NULL_ARG, "indexer_topk: scores and idx are required");
+    if (B <= 0 || S <= 0 || N <= 0 || K <= 0 || ratio <= 0)
+        return fail(SD_ERR_BAD_SHAPE, "indexer_topk: sizes must be positive (B=%d S=%d N=%d K=%d ratio=%d)", B, S, N, K,
+                    ratio);
+    if (N > sd::kMaxTopkN || K > sd::kMaxTopkK)
+        return fail(SD_ERR_UNSUPPORTED, "indexer_topk: N=%d and K=%d must be at most %d and %d", N, K, sd::kMaxTopkN,
+                    sd::kMaxTopkK);
+    int st = check_grid("indexer_topk", ((int64_t)B * S + 3) / 4, 256, "B*S must be below 2^26");
+    if (st != SD_OK) return st;
+    return hip_status(sd::launch_indexer_topk(scores, seg, B, S, N, K, ratio, idx, values, stream),
+                      "indexer_topk launch");
+}
+
+int indexer_topk_bwd(const float *dvalues, const int32_t *idx, int B, int S, int N, int K, float *dscores,
+                     hipStream_t stream) {
+    if (!dvalues || !idx || !dscores)
+        return fail(SD_ERR_NULL_ARG, "indexer_topk_bwd: dvalues, idx and dscores are required");
+    if (B <= 0 || S <= 0 || N <= 0 || K <= 0)
+        return fail(SD_ERR_BAD_SHAPE, "indexer_topk_bwd: sizes must be positive (B=%d S=%d N=%d K=%d)", B, S, N, K);
+    if (N > sd::kMaxTopkN || K > sd::kMaxTopkK)
+        return fail(SD_ERR_UNSUPPORTED, "indexer_topk_bwd: N=%d and K=%d must be at most %d and %d", N, K,
+                    sd::kMaxTopkN, sd::kMaxTopkK);
+    int st = check_grid("indexer_topk_bwd", ((int64_t)B * S + 3) / 4, 256, "B*S must be below 2^26");
+    if (st != SD_OK) return st;
+    return hip_status(sd::launch_indexer_topk_bwd(dvalues, idx, B, S, N, K, dscores, stream),
+                      "indexer_topk_bwd launch");
+}
+
 int distill_kl_fwd_bwd_noalloc(const float *target, const float *logits, const int32_t *idx, int B, int S, int K,
                                int N, float grad_scale, float *kl_rows, float *dlogits, float *stats,
                                hipStream_t stream) {

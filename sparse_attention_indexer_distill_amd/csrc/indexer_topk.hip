@@ -1,0 +1,223 @@
+// indexer_topk.hip -- the indexer's masked top-k selection and its gradient, on gfx950.
+//
+// The step before the distillation target (MaxText PR "Add Indexer Loss [Deepseek v4]"):
+// each query keeps the top-k of its student block scores under the causal block mask
+// combined with the segment (packing) mask -- a block is visible to token t once it is
+// complete at t and all of its tokens belong to t's document -- and the slots it cannot
+// fill hold -1.  Kept blocks are written in ascending block order (the set is what the
+// target and the KL use; ascending order also makes later row gathers walk memory
+// forward), with their scores as the values (the student logits of the KL); a -1 slot's
+// value is -inf.  Equal scores prefer the smaller block index; NaN ranks lowest.
+//
+// Mapping: one wave per (b,t) row, element n of the row on lane n % 64, register n / 64,
+// so every load and every ordered prefix runs over 64 consecutive blocks.  Scores map to
+// order-preserving 32-bit keys (NaN -> 0, the smallest); the K-th largest visible key is
+// found most-significant bit first, one wave-wide count per bit (a compare per element,
+// then ballot population counts on the scalar unit), so no sort and no LDS are needed.
+// The backward is the adjoint of the gather values[k] = scores[idx[k]]: a dense row of N
+// gradients, built in LDS and streamed out with 16-byte stores.
+#include <math.h>
+
+#include "sd_device.hpp"
+#include "sd_internal.hpp"
+
+namespace sd {
+namespace {
+
+constexpr int kTopkWaves = 4;  // rows per workgroup, one wave each
+
+// Order-preserving key of a score: larger score -> larger key; -0 and +0 share a key; every
+// NaN maps to 0, below -inf (whose key is 0x007fffff).
+__device__ __forceinline__ uint32_t order_key(float s) {
+    uint32_t b = __float_as_uint(s);
+    if ((b & 0x7fffffffu) > 0x7f800000u) return 0u;
+    if (b == 0x80000000u) b = 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ int wave_popc(bool p) { return __popcll(__ballot(p)); }
+
+// A wave's LDS accesses execute in issue order, so a lane reads what another lane of the same
+// wave stored by an earlier instruction; this keeps the compiler from moving LDS accesses
+// across the point and waits for the stores to complete.
+__device__ __forceinline__ void wave_lds_order() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+}
+
+// lanes below this one whose predicate is set (exclusive prefix within the wave)
+__device__ __forceinline__ int wave_prefix(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// E: registers per lane (N <= 64 E).
+template <int E>
+__global__ __launch_bounds__(kTopkWaves * 64) void indexer_topk_kernel(
+    const float *__restrict__ scores, const int32_t *__restrict__ seg, int64_t rows, int S, int N, int K, int ratio,
+    int32_t *__restrict__ idx_out, float *__restrict__ val_out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kTopkWaves + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int64_t b = row / S;
+    const int t = (int)(row - b * S);
+    const int ncomplete = (t + 1) / ratio;           // blocks complete at t
+    const int nc = ncomplete < N ? ncomplete : N;
+    const float *sc = scores + row * N;
+    const int32_t *sg = seg ? seg + b * S : nullptr;
+    const int32_t st = sg ? sg[t] : 0;
+
+    uint32_t key[E];
+    bool vis[E];
+    float val[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int n = 64 * e + lane;
+        bool v = n < nc;
+        if (v && sg) {
+            for (int i = 0; i < ratio; ++i) v = v && sg[ratio * n + i] == st;   // whole block in t's document
+        }
+        val[e] = v ? sc[n] : 0.f;
+        vis[e] = v;
+        key[e] = v ? order_key(val[e]) : 0u;
+    }
+    int count = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) count += wave_popc(vis[e]);
+
+    // Threshold: the K-th largest visible key (a visible key counts when it is >= cand, and
+    // cand >= 1 never admits an invisible one, whose key is 0).
+    uint32_t tau = 0u;
+    int need = count;  // how many of the keys equal to tau are kept (in ascending block order)
+    if (count > K) {
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = tau | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) cnt += wave_popc(key[e] >= cand);
+            if (cnt >= K) tau = cand;
+        }
+        int greater = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) greater += wave_popc(vis[e] && key[e] > tau);
+        need = K - greater;
+    }
+
+    int32_t *io = idx_out + row * K;
+    float *vo = val_out ? val_out + row * K : nullptr;
+    int tie_base = 0, pos_base = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        bool sel = vis[e];
+        if (count > K) {
+            const bool tie = vis[e] && key[e] == tau;
+            const uint64_t tm = __ballot(tie);
+            sel = vis[e] && (key[e] > tau || (tie && tie_base + wave_prefix(tm) < need));
+            tie_base += __popcll(tm);
+        }
+        const uint64_t sm = __ballot(sel);
+        if (sel) {
+            const int pos = pos_base + wave_prefix(sm);
+            io[pos] = 64 * e + lane;
+            if (vo) vo[pos] = val[e];
+        }
+        pos_base += __popcll(sm);
+    }
+    for (int k = pos_base + lane; k < K; k += 64) {  // slots left over
+        io[k] = -1;
+        if (vo) vo[k] = -INFINITY;
+    }
+}
+
+// dscores[row, n] = sum of dval[row, k] over the valid slots k holding n, in slot order; 0 for
+// every other block.  Slot indices are first written into the wave's LDS row as tags: if every
+// valid slot reads its own tag back, the row's slots are distinct and each block receives
+// one gradient by a plain store; otherwise the gradients are added one slot at a time.
+__global__ __launch_bounds__(kTopkWaves * 64) void indexer_topk_bwd_kernel(
+    const float *__restrict__ dval, const int32_t *__restrict__ idx, int64_t rows, int N, int K,
+    float *__restrict__ dscores) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kTopkWaves + w;
+    if (row >= rows) return;  // waves never meet at a workgroup barrier: each owns its LDS row
+    uint32_t *tag = reinterpret_cast<uint32_t *>(smem) + (size_t)w * N;
+    float *buf = reinterpret_cast<float *>(tag);
+    const int32_t *ir = idx + row * K;
+    const float *dr = dval + row * K;
+
+    for (int n = lane; n < N; n += 64) tag[n] = 0xffffffffu;
+    wave_lds_order();
+    for (int k = lane; k < K; k += 64) {
+        const int n = ir[k];
+        if (n >= 0 && n < N) tag[n] = (uint32_t)k;
+    }
+    wave_lds_order();
+    bool dup = false;
+    for (int k = lane; k < K; k += 64) {
+        const int n = ir[k];
+        if (n >= 0 && n < N) dup = dup || tag[n] != (uint32_t)k;
+    }
+    const bool any_dup = __ballot(dup) != 0;
+    wave_lds_order();
+    for (int n = lane; n < N; n += 64) buf[n] = 0.f;
+    wave_lds_order();
+    if (!any_dup) {
+        for (int k = lane; k < K; k += 64) {
+            const int n = ir[k];
+            if (n >= 0 && n < N) buf[n] = dr[k];
+        }
+    } else {
+        for (int k0 = 0; k0 < K; k0 += 64) {
+            const int k = k0 + lane;
+            const int n = k < K ? ir[k] : -1;
+            const float g = k < K ? dr[k] : 0.f;
+            for (int j = 0; j < 64; ++j) {  // slot order within the chunk
+                if (lane == j && n >= 0 && n < N) buf[n] += g;
+                wave_lds_order();
+            }
+        }
+    }
+    wave_lds_order();
+    float *o = dscores + row * N;
+    if ((N & 3) == 0) {
+        for (int n = 4 * lane; n < N; n += 256)
+            *reinterpret_cast<f32x4 *>(o + n) = *reinterpret_cast<const f32x4 *>(buf + n);
+    } else {
+        for (int n = lane; n < N; n += 64) o[n] = buf[n];
+    }
+}
+
+template <int E>
+hipError_t launch_topk(const float *scores, const int32_t *seg, int64_t rows, int S, int N, int K, int ratio,
+                       int32_t *idx, float *values, hipStream_t stream) {
+    const unsigned grid = (unsigned)((rows + kTopkWaves - 1) / kTopkWaves);
+    hipLaunchKernelGGL(indexer_topk_kernel<E>, dim3(grid), dim3(kTopkWaves * 64), 0, stream, scores, seg, rows, S,
+                       N, K, ratio, idx, values);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_indexer_topk(const float *scores, const int32_t *seg, int B, int S, int N, int K, int ratio,
+                               int32_t *idx, float *values, hipStream_t stream) {
+    const int64_t rows = (int64_t)B * S;
+    if (N <= 64) return launch_topk<1>(scores, seg, rows, S, N, K, ratio, idx, values, stream);
+    if (N <= 128) return launch_topk<2>(scores, seg, rows, S, N, K, ratio, idx, values, stream);
+    if (N <= 256) return launch_topk<4>(scores, seg, rows, S, N, K, ratio, idx, values, stream);
+    if (N <= 512) return launch_topk<8>(scores, seg, rows, S, N, K, ratio, idx, values, stream);
+    if (N <= 1024) return launch_topk<16>(scores, seg, rows, S, N, K, ratio, idx, values, stream);
+    if (N <= 2048) return launch_topk<32>(scores, seg, rows, S, N, K, ratio, idx, values, stream);
+    return launch_topk<64>(scores, seg, rows, S, N, K, ratio, idx, values, stream);
+}
+
+hipError_t launch_indexer_topk_bwd(const float *dvalues, const int32_t *idx, int B, int S, int N, int K,
+                                   float *dscores, hipStream_t stream) {
+    const int64_t rows = (int64_t)B * S;
+    const unsigned grid = (unsigned)((rows + kTopkWaves - 1) / kTopkWaves);
+    const size_t lds = (size_t)kTopkWaves * N * sizeof(float);  // <= 64 KiB for N <= 4096
+    hipLaunchKernelGGL(indexer_topk_bwd_kernel, dim3(grid), dim3(kTopkWaves * 64), lds, stream, dvalues, idx, rows,
+                       N, K, dscores);
+    return hipGetLastError();
+}
+
+}  // namespace sd

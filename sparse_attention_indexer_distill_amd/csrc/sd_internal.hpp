@@ -61,4 +61,11 @@ hipError_t launch_distill_kl(const float *target, const float *logits, const int
                              int K, int N, float grad_scale, float *kl_rows, float *dlogits, float *stats,
                              void *workspace, hipStream_t stream);
 
+constexpr int kMaxTopkN = 4096;
+constexpr int kMaxTopkK = 4096;
+hipError_t launch_indexer_topk(const float *scores, const int32_t *seg, int B, int S, int N, int K, int ratio,
+                               int32_t *idx, float *values, hipStream_t stream);
+hipError_t launch_indexer_topk_bwd(const float *dvalues, const int32_t *idx, int B, int S, int N, int K,
+                                   float *dscores, hipStream_t stream);
+
 }  // namespace sd

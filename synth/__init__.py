@@ -27,7 +27,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-TENSOR_ID = dict(q=1, pool=2, kwin=3, sink=4, idx=5, logits=6, seg=7, rowpick=8)
+TENSOR_ID = dict(q=1, pool=2, kwin=3, sink=4, idx=5, logits=6, seg=7, rowpick=8, scores=9, kv=10, cscore=11, ape=12,
+                 dout=13)
 COMPRESS_RATIO = 4
 
 
@@ -147,6 +148,17 @@ def duplicate_slots(idx: np.ndarray, N: int, seed: int) -> np.ndarray:
             elif len(v) == 1 and K > 1:
                 d[b, t, (v[0] + 1) % K] = d[b, t, v[0]]
     return d
+
+
+def student_scores(cfg: Config | str, ties: bool = False) -> torch.Tensor:
+    """[B,S,N] float32 student block scores, N(0,1); with ties=True floor(2x), so only a
+    dozen distinct values occur and top-k thresholds fall inside groups of equal scores."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    s = _normal(rng_for(cfg, "scores"), (cfg.B, cfg.S, cfg.N))
+    if ties:
+        s = np.floor(2.0 * s).astype(np.float32)
+    return torch.from_numpy(s)
 
 
 def make_inputs(cfg: Config | str, shuffle_pad: bool = False) -> dict:

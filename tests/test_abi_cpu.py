@@ -34,7 +34,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("window_lse", "distill_target", "distill_target_fused", "distill_kl_fwd_bwd",
-              "distill_kl_workspace_bytes", "distill_kl_fwd_bwd_noalloc", "sd_status_string", "sd_last_error"):
+              "distill_kl_workspace_bytes", "distill_kl_fwd_bwd_noalloc", "indexer_topk", "indexer_topk_bwd",
+              "sd_status_string", "sd_last_error"):
         assert n in names, names
 
 
@@ -178,6 +179,27 @@ def test_noalloc_kl_rejections(lib):
     assert call(B=1, S=(1 << 21) + 1) == sd.SD_ERR_UNSUPPORTED
     assert b"2097152 rows" in lib.sd_last_error()
     assert call(B=2, S=(1 << 20) + 8) == sd.SD_ERR_UNSUPPORTED
+
+
+def test_indexer_topk_rejections(lib):
+    def topk(scores=FAKE, idx=FAKE, B=1, S=8, N=4, K=2, ratio=4):
+        return lib.indexer_topk(scores, None, B, S, N, K, ratio, idx, None, None)
+
+    def bwd(dv=FAKE, idx=FAKE, out=FAKE, B=1, S=8, N=4, K=2):
+        return lib.indexer_topk_bwd(dv, idx, B, S, N, K, out, None)
+    assert topk(scores=None) == sd.SD_ERR_NULL_ARG
+    assert topk(idx=None) == sd.SD_ERR_NULL_ARG
+    assert topk(N=0) == sd.SD_ERR_BAD_SHAPE
+    assert topk(ratio=0) == sd.SD_ERR_BAD_SHAPE
+    assert topk(K=-1) == sd.SD_ERR_BAD_SHAPE
+    assert topk(N=4097) == sd.SD_ERR_UNSUPPORTED
+    assert topk(K=4097) == sd.SD_ERR_UNSUPPORTED
+    assert topk(B=1, S=1 << 26) == sd.SD_ERR_UNSUPPORTED           # 256 lanes per 4 rows
+    assert b"2^32 - 1" in lib.sd_last_error()
+    assert bwd(dv=None) == sd.SD_ERR_NULL_ARG
+    assert bwd(out=None) == sd.SD_ERR_NULL_ARG
+    assert bwd(S=0) == sd.SD_ERR_BAD_SHAPE
+    assert bwd(N=5000) == sd.SD_ERR_UNSUPPORTED
 
 
 def test_binding_rejects_host_tensors():

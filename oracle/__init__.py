@@ -55,6 +55,8 @@ def _load():
                                  [ctypes.c_double, _lp, ctypes.c_int64, _dp, _dp, _dp]
         lib.oracle_indexer_topk.argtypes = [_fp, _ip] + [ctypes.c_int] * 5 + [_lp, ctypes.c_int64, _ip, _fp]
         lib.oracle_indexer_topk_bwd.argtypes = [_fp, _ip] + [ctypes.c_int] * 4 + [_lp, ctypes.c_int64, _dp]
+        lib.oracle_compressor_pool.argtypes = [_fp, _fp, _fp, _ip] + [ctypes.c_int] * 5 + [_dp]
+        lib.oracle_compressor_pool_bwd.argtypes = [_fp, _fp, _fp, _ip, _fp] + [ctypes.c_int] * 5 + [_dp, _dp, _dp]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = lib
@@ -194,3 +196,41 @@ def indexer_topk_bwd(dval, idx, N: int, rows=None):
     out = np.empty((n, N), dtype=np.float64)
     _load().oracle_indexer_topk_bwd(dp, ip, B, S, int(N), K, rp, n, out.ctypes.data_as(_dp))
     return out
+
+
+def compressor_pool(kv, score, ape, seg, ratio: int, overlap: bool):
+    """pool[b,n,d] = sum_i softmax_i(score[b,j_i,d] + ape[i,d]) kv[b,j_i,d] over the present
+    positions of entry n's window: tokens ratio*n .. ratio*n+ratio-1 (overlap False), or
+    ratio*(n-1) .. ratio*n+ratio-1 (overlap True; positions before token 0 absent); a
+    position whose token has another segment than the entry's last token is absent.
+    kv, score [B,S,D]; ape [Wc,D]; seg [B,S] or None.  Returns float64 [B, S//ratio, D]."""
+    ka, kp = _f32(kv)
+    B, S, D = ka.shape
+    sa, sp = _f32(score)
+    aa, ap = _f32(ape)
+    ga, gp = _i32(seg)
+    Wc = ratio * (2 if overlap else 1)
+    assert aa.shape == (Wc, D) and sa.shape == ka.shape
+    out = np.empty((B, S // ratio, D), dtype=np.float64)
+    _load().oracle_compressor_pool(kp, sp, ap, gp, B, S, D, int(ratio), int(bool(overlap)),
+                                   out.ctypes.data_as(_dp))
+    return out
+
+
+def compressor_pool_bwd(kv, score, ape, seg, dpool, ratio: int, overlap: bool):
+    """Analytic backward of compressor_pool for dpool [B,N,D]: returns float64 (dkv [B,S,D],
+    dscore [B,S,D], dape [Wc,D])."""
+    ka, kp = _f32(kv)
+    B, S, D = ka.shape
+    sa, sp = _f32(score)
+    aa, ap = _f32(ape)
+    ga, gp = _i32(seg)
+    da, dp = _f32(dpool)
+    Wc = ratio * (2 if overlap else 1)
+    assert da.shape == (B, S // ratio, D)
+    dkv = np.empty((B, S, D), dtype=np.float64)
+    dsc = np.empty((B, S, D), dtype=np.float64)
+    dape = np.empty((Wc, D), dtype=np.float64)
+    _load().oracle_compressor_pool_bwd(kp, sp, ap, gp, dp, B, S, D, int(ratio), int(bool(overlap)),
+                                       dkv.ctypes.data_as(_dp), dsc.ctypes.data_as(_dp), dape.ctypes.data_as(_dp))
+    return dkv, dsc, dape

@@ -334,3 +334,114 @@ void oracle_indexer_topk_bwd(const float *dval, const int32_t *idx, int B, int S
         }
     }
 }
+
+/* ----------------------------------------------------------------------------------
+ * Compressor pool, the step that builds the compressed rows ([P2] Primus PR "Docker Build
+ * for DeepSeek-v4 (Don't Merge)", commit fusing the compressed-attention small kernels:
+ * compressor_pool fuses score+ape, a softmax over the window and the weighted sum, with an
+ * analytic backward for kv, score and ape; HCA windows do not overlap, CSA windows do).
+ *
+ * Readings (the page gives the steps, not the shapes):
+ *   kv, score: [B,S,D] per-token values and compression logits; ape: [Wc,D], a learned
+ *   bias per window position and channel; ratio r; entry n (n < N = floor(S/r)) pools
+ *     HCA (overlap 0): tokens r*n .. r*n + r - 1                     (Wc = r)
+ *     CSA (overlap 1): tokens r*(n-1) .. r*n + r - 1, its own block and the one before
+ *                      (Wc = 2r; positions before token 0 are absent)
+ *   position i of entry n is token j = r*n - overlap*r + i; it is present iff j >= 0 and
+ *   seg[j] equals the segment of the entry's last token (seg == NULL: one segment).
+ *   For each channel d, over the present positions:
+ *     w_i = softmax_i(score[j_i,d] + ape[i,d]);   pool[n,d] = sum_i w_i kv[j_i,d]
+ * out pool: [B,N,D] */
+static int cp_token(int n, int i, int r, int overlap) { return r * n - overlap * r + i; }
+
+static int cp_present(const int32_t *seg_b, int S, int n, int i, int r, int overlap) {
+    int j = cp_token(n, i, r, overlap);
+    if (j < 0 || j >= S) return 0;
+    if (seg_b && seg_b[j] != seg_b[r * n + r - 1]) return 0;
+    return 1;
+}
+
+void oracle_compressor_pool(const float *kv, const float *score, const float *ape, const int32_t *seg,
+                            int B, int S, int D, int r, int overlap, double *pool) {
+    const int N = S / r, Wc = r * (1 + overlap);
+    #pragma omp parallel
+    {
+        double *l = (double *)malloc(sizeof(double) * (size_t)Wc);
+        #pragma omp for schedule(static)
+        for (int64_t bn = 0; bn < (int64_t)B * N; ++bn) {
+            int64_t b = bn / N;
+            int n = (int)(bn % N);
+            const int32_t *seg_b = seg ? seg + b * S : NULL;
+            for (int d = 0; d < D; ++d) {
+                double m = -INFINITY;
+                for (int i = 0; i < Wc; ++i) {
+                    if (!cp_present(seg_b, S, n, i, r, overlap)) continue;
+                    int64_t j = cp_token(n, i, r, overlap);
+                    l[i] = (double)score[(b * S + j) * D + d] + (double)ape[(int64_t)i * D + d];
+                    if (l[i] > m) m = l[i];
+                }
+                double den = 0.0, num = 0.0;
+                for (int i = 0; i < Wc; ++i) {
+                    if (!cp_present(seg_b, S, n, i, r, overlap)) continue;
+                    int64_t j = cp_token(n, i, r, overlap);
+                    double e = exp(l[i] - m);
+                    den += e;
+                    num += e * (double)kv[(b * S + j) * D + d];
+                }
+                pool[bn * D + d] = num / den;
+            }
+        }
+        free(l);
+    }
+}
+
+/* Analytic backward of oracle_compressor_pool for an upstream gradient dpool [B,N,D]:
+ *   dkv[j,d]    = sum over entries n containing j:  w_{n,i(j),d} dpool[n,d]
+ *   dscore[j,d] = sum over entries n containing j:  w_{n,i(j),d} (kv[j,d] - pool[n,d]) dpool[n,d]
+ *   dape[i,d]   = sum over b and n with position i present: the same product
+ * (the softmax Jacobian diag(w) - w w^T applied to the kv-weighted gradient).  Tokens in no
+ * entry (the tail past N*r, or absent positions) get 0.
+ * out dkv, dscore: [B,S,D]; dape: [Wc,D] */
+void oracle_compressor_pool_bwd(const float *kv, const float *score, const float *ape, const int32_t *seg,
+                                const float *dpool, int B, int S, int D, int r, int overlap,
+                                double *dkv, double *dscore, double *dape) {
+    const int N = S / r, Wc = r * (1 + overlap);
+    for (int64_t x = 0; x < (int64_t)B * S * D; ++x) dkv[x] = dscore[x] = 0.0;
+    for (int64_t x = 0; x < (int64_t)Wc * D; ++x) dape[x] = 0.0;
+    double *w = (double *)malloc(sizeof(double) * (size_t)Wc);
+    /* sequential over entries: several entries add into the same token and position */
+    for (int64_t b = 0; b < B; ++b) {
+        const int32_t *seg_b = seg ? seg + b * S : NULL;
+        for (int n = 0; n < N; ++n) {
+            for (int d = 0; d < D; ++d) {
+                double m = -INFINITY;
+                for (int i = 0; i < Wc; ++i) {
+                    if (!cp_present(seg_b, S, n, i, r, overlap)) continue;
+                    int64_t j = cp_token(n, i, r, overlap);
+                    w[i] = (double)score[(b * S + j) * D + d] + (double)ape[(int64_t)i * D + d];
+                    if (w[i] > m) m = w[i];
+                }
+                double den = 0.0;
+                for (int i = 0; i < Wc; ++i)
+                    if (cp_present(seg_b, S, n, i, r, overlap)) den += exp(w[i] - m);
+                double p = 0.0;
+                for (int i = 0; i < Wc; ++i) {
+                    if (!cp_present(seg_b, S, n, i, r, overlap)) continue;
+                    int64_t j = cp_token(n, i, r, overlap);
+                    w[i] = exp(w[i] - m) / den;
+                    p += w[i] * (double)kv[(b * S + j) * D + d];
+                }
+                double g = (double)dpool[(b * N + n) * (int64_t)D + d];
+                for (int i = 0; i < Wc; ++i) {
+                    if (!cp_present(seg_b, S, n, i, r, overlap)) continue;
+                    int64_t j = cp_token(n, i, r, overlap);
+                    double kvj = (double)kv[(b * S + j) * D + d];
+                    dkv[(b * S + j) * D + d] += w[i] * g;
+                    dscore[(b * S + j) * D + d] += w[i] * (kvj - p) * g;
+                    dape[(int64_t)i * D + d] += w[i] * (kvj - p) * g;
+                }
+            }
+        }
+    }
+    free(w);
+}

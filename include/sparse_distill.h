@@ -210,6 +210,51 @@ int indexer_topk_bwd(const float *dvalues, const int32_t *idx, int B, int S, int
                      float *dscores, hipStream_t stream);
 
 /*
+ * compressor_pool -- the compressor that builds the compressed rows the target gathers.
+ *
+ *   Entry n (n < N = floor(S / ratio)) pools the Wc = ratio * (1 + overlap) tokens
+ *   j = ratio*n - overlap*ratio + i, i < Wc, of its batch row: its own block, and with
+ *   overlap the block before it too (position i is absent when j < 0, or when token j's
+ *   segment differs from that of the entry's last token, ratio*n + ratio - 1):
+ *     w_i        = softmax over the present i of (score[b,j,d] + ape[i,d]), per channel d
+ *     pool[b,n,d] = sum_i w_i kv[b,j,d]
+ *
+ * Defined by the Primus PR "Docker Build for DeepSeek-v4 (Don't Merge)", commit fusing the
+ * compressed-attention small kernels: score + ape, softmax over the window and the weighted
+ * sum in one launch; HCA windows (overlap 0, e.g. ratio 128) do not overlap, CSA windows
+ * (overlap 1, ratio 4) do.  ape carries one bias per window position and channel.
+ *
+ *   kv, score [B,S,D] dtype;  ape [Wc,D] float32;  seg [B,S] int32 or NULL
+ *   pool [B,N,D] float32 out
+ * Limits: D % 4 == 0; ratio a power of two, <= 128 without overlap, <= 16 with it; S >=
+ * ratio; every array 16-byte aligned (SD_ERR_BAD_SHAPE otherwise); B * N * D < 2^32.
+ */
+int compressor_pool(const void *kv, const void *score, const float *ape, const int32_t *seg,
+                    int B, int S, int D, int ratio, int overlap, int dtype, float *pool,
+                    hipStream_t stream);
+
+/*
+ * compressor_pool_bwd -- the analytic backward of compressor_pool for an upstream dpool.
+ *
+ *   dkv[b,j,d]    = sum over the entries n holding j:  w dpool[b,n,d]
+ *   dscore[b,j,d] = sum over the entries n holding j:  w (kv[b,j,d] - pool[b,n,d]) dpool[b,n,d]
+ *   dape[i,d]     = sum over b and n of the same product at position i
+ * (the softmax Jacobian applied to the kv-weighted gradient; same commit: "analytic
+ * backward").  Tokens held by no entry (past N * ratio, or absent) get 0.  pool is
+ * recomputed, not read.
+ *
+ *   dpool [B,N,D] float32;  dkv, dscore [B,S,D] float32 out;  dape [Wc,D] float32 out
+ *   workspace: compressor_pool_bwd_workspace_bytes(B,S,D,ratio,overlap) bytes of caller
+ *   device memory, 16-byte aligned; no initialisation needed; calls sharing it must be ordered.
+ * Limits: those of compressor_pool.
+ */
+size_t compressor_pool_bwd_workspace_bytes(int B, int S, int D, int ratio, int overlap);
+int compressor_pool_bwd(const void *kv, const void *score, const float *ape, const int32_t *seg,
+                        const float *dpool, int B, int S, int D, int ratio, int overlap,
+                        int dtype, float *dkv, float *dscore, float *dape, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/*
  * distill_kl_fwd_bwd_noalloc -- distill_kl_fwd_bwd without a workspace argument, for callers
  * that cannot allocate device memory: code under HIP graph capture, tight serving loops and
  * harnesses that forbid hipMalloc.  Same arguments, results and limits as distill_kl_fwd_bwd

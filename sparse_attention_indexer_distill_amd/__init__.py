@@ -24,7 +24,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["window_lse", "distill_target", "distill_target_fused", "distill_kl_fwd_bwd", "distill_kl_workspace_bytes",
-           "distill_kl_fwd_bwd_noalloc", "indexer_topk", "indexer_topk_bwd", "csa_distill_layer", "library_path", "load_library", "SD_BF16", "SD_F32"]
+           "distill_kl_fwd_bwd_noalloc", "indexer_topk", "indexer_topk_bwd", "compressor_pool", "compressor_pool_bwd",
+           "compressor_pool_bwd_workspace_bytes", "csa_distill_layer", "library_path", "load_library", "SD_BF16", "SD_F32"]
 
 SD_OK, SD_ERR_NULL_ARG, SD_ERR_BAD_SHAPE, SD_ERR_UNSUPPORTED, SD_ERR_DTYPE, SD_ERR_HIP = range(6)
 SD_BF16, SD_F32 = 0, 1
@@ -68,6 +69,13 @@ def load_library():
     lib.indexer_topk.restype = _i
     lib.indexer_topk_bwd.argtypes = [_vp, _vp, _i, _i, _i, _i, _vp, _vp]
     lib.indexer_topk_bwd.restype = _i
+    lib.compressor_pool.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp]
+    lib.compressor_pool.restype = _i
+    lib.compressor_pool_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+    lib.compressor_pool_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.compressor_pool_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
+                                        ctypes.c_size_t, _vp]
+    lib.compressor_pool_bwd.restype = _i
     lib.sd_status_string.argtypes = [_i]
     lib.sd_status_string.restype = ctypes.c_char_p
     lib.sd_last_error.argtypes = []
@@ -399,6 +407,72 @@ def indexer_topk_bwd(dvalues: torch.Tensor, idx: torch.Tensor, N: int, *, out: O
     st = lib.indexer_topk_bwd(_ptr(dvalues), _ptr(idx), B, S, int(N), K, _ptr(out), _stream(dev, stream))
     _check(st, "indexer_topk_bwd")
     return out
+
+
+def _compressor_inputs(kv, score, ape, seg, ratio, overlap):
+    dev = kv.device
+    kv = _dev(kv, "kv", dev)
+    score = _dev(score, "score", dev)
+    if kv.dim() != 3 or score.shape != kv.shape or score.dtype != kv.dtype:
+        raise ValueError("kv and score must share one [B,S,D] shape and dtype")
+    B, S, D = kv.shape
+    Wc = int(ratio) * (2 if overlap else 1)
+    ape = _dev(ape.detach().to(torch.float32), "ape", dev)
+    if tuple(ape.shape) != (Wc, D):
+        raise ValueError(f"ape must be [{Wc},{D}] (window positions x channels), got {tuple(ape.shape)}")
+    if seg is not None:
+        seg = _dev(seg.to(torch.int32), "seg", dev)
+        if seg.shape != (B, S):
+            raise ValueError(f"seg must be [{B},{S}]")
+    return dev, kv, score, ape, seg, B, S, D
+
+
+@_on_stream
+def compressor_pool(kv: torch.Tensor, score: torch.Tensor, ape: torch.Tensor, seg: Optional[torch.Tensor] = None, *,
+                    ratio: int, overlap: bool, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """pool [B, S//ratio, D] fp32: per channel, the softmax over each entry's window of
+    score + ape, weighting kv (windows of ratio tokens; with overlap, two blocks)."""
+    lib = load_library()
+    dev, kv, score, ape, seg, B, S, D = _compressor_inputs(kv, score, ape, seg, ratio, overlap)
+    N = S // int(ratio)
+    if out is None:
+        out = torch.empty((B, N, D), dtype=torch.float32, device=dev)
+    else:
+        _out(out, "out", (B, N, D), dev)
+    st = lib.compressor_pool(_ptr(kv), _ptr(score), _ptr(ape), _ptr(seg), B, S, D, int(ratio), int(bool(overlap)),
+                             _dtype_code(kv), _ptr(out), _stream(dev, stream))
+    _check(st, "compressor_pool")
+    return out
+
+
+def compressor_pool_bwd_workspace_bytes(B: int, S: int, D: int, ratio: int, overlap: bool) -> int:
+    return int(load_library().compressor_pool_bwd_workspace_bytes(B, S, D, int(ratio), int(bool(overlap))))
+
+
+@_on_stream
+def compressor_pool_bwd(kv: torch.Tensor, score: torch.Tensor, ape: torch.Tensor, dpool: torch.Tensor,
+                        seg: Optional[torch.Tensor] = None, *, ratio: int, overlap: bool,
+                        dkv: Optional[torch.Tensor] = None, dscore: Optional[torch.Tensor] = None,
+                        dape: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        stream=None):
+    """Analytic backward of compressor_pool: (dkv [B,S,D], dscore [B,S,D], dape [Wc,D]), fp32."""
+    lib = load_library()
+    dev, kv, score, ape, seg, B, S, D = _compressor_inputs(kv, score, ape, seg, ratio, overlap)
+    N = S // int(ratio)
+    Wc = ape.shape[0]
+    dpool = _dev(dpool, "dpool", dev)
+    if tuple(dpool.shape) != (B, N, D) or dpool.dtype != torch.float32:
+        raise ValueError(f"dpool must be float32 [{B},{N},{D}]")
+    dkv = torch.empty((B, S, D), dtype=torch.float32, device=dev) if dkv is None else _out(dkv, "dkv", (B, S, D), dev)
+    dscore = torch.empty((B, S, D), dtype=torch.float32, device=dev) if dscore is None else \
+        _out(dscore, "dscore", (B, S, D), dev)
+    dape = torch.empty((Wc, D), dtype=torch.float32, device=dev) if dape is None else _out(dape, "dape", (Wc, D), dev)
+    workspace = _workspace(workspace, compressor_pool_bwd_workspace_bytes(B, S, D, ratio, overlap), dev)
+    st = lib.compressor_pool_bwd(_ptr(kv), _ptr(score), _ptr(ape), _ptr(seg), _ptr(dpool), B, S, D, int(ratio),
+                                 int(bool(overlap)), _dtype_code(kv), _ptr(dkv), _ptr(dscore), _ptr(dape),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev, stream))
+    _check(st, "compressor_pool_bwd")
+    return dkv, dscore, dape
 
 
 @_on_stream

@@ -192,6 +192,62 @@ int indexer_topk_bwd(const float *dvalues, const int32_t *idx, int B, int S, int
                       "indexer_topk_bwd launch");
 }
 
+namespace {
+
+// Shared checks of the compressor entry points (sizes, dtype, supported windows, alignment of
+// the 16-byte vector accesses, grid size).
+int check_compressor(const char *fn, int B, int S, int D, int ratio, int overlap, int dtype,
+                     const void *const *ptrs, int nptrs) {
+    if (dtype != SD_BF16 && dtype != SD_F32) return fail(SD_ERR_DTYPE, "%s: unknown dtype code %d", fn, dtype);
+    if (B <= 0 || S <= 0 || D <= 0 || ratio <= 0 || (overlap != 0 && overlap != 1))
+        return fail(SD_ERR_BAD_SHAPE, "%s: sizes must be positive and overlap 0 or 1 (B=%d S=%d D=%d ratio=%d "
+                    "overlap=%d)", fn, B, S, D, ratio, overlap);
+    if (S < ratio) return fail(SD_ERR_BAD_SHAPE, "%s: S=%d holds no complete block of %d tokens", fn, S, ratio);
+    if (D % 4 != 0) return fail(SD_ERR_UNSUPPORTED, "%s: D=%d must be a multiple of 4", fn, D);
+    if (!sd::compressor_supported(ratio, overlap))
+        return fail(SD_ERR_UNSUPPORTED, "%s: ratio=%d with overlap=%d is not covered (powers of two up to 128 "
+                    "without overlap, up to 16 with overlap)", fn, ratio, overlap);
+    for (int i = 0; i < nptrs; ++i)
+        if (ptrs[i] && (uintptr_t)ptrs[i] % 16 != 0)
+            return fail(SD_ERR_BAD_SHAPE, "%s: array argument %d is not 16-byte aligned", fn, i);
+    return check_grid(fn, ((int64_t)B * (S / ratio) * D + 255) / 256, 256, "B*(S/ratio)*D must be below 2^32");
+}
+
+}  // namespace
+
+int compressor_pool(const void *kv, const void *score, const float *ape, const int32_t *seg, int B, int S, int D,
+                    int ratio, int overlap, int dtype, float *pool, hipStream_t stream) {
+    if (!kv || !score || !ape || !pool)
+        return fail(SD_ERR_NULL_ARG, "compressor_pool: kv, score, ape and pool are required");
+    const void *ptrs[] = {kv, score, ape, pool};
+    int st = check_compressor("compressor_pool", B, S, D, ratio, overlap, dtype, ptrs, 4);
+    if (st != SD_OK) return st;
+    return hip_status(sd::launch_compressor_pool(kv, score, ape, seg, B, S, D, ratio, overlap, dtype, pool, stream),
+                      "compressor_pool launch");
+}
+
+size_t compressor_pool_bwd_workspace_bytes(int B, int S, int D, int ratio, int overlap) {
+    if (B <= 0 || S <= 0 || D <= 0 || ratio <= 0 || S < ratio || (overlap != 0 && overlap != 1)) return 0;
+    return sd::compressor_bwd_workspace_bytes(B, S, D, ratio, overlap);
+}
+
+int compressor_pool_bwd(const void *kv, const void *score, const float *ape, const int32_t *seg, const float *dpool,
+                        int B, int S, int D, int ratio, int overlap, int dtype, float *dkv, float *dscore, float *dape,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!kv || !score || !ape || !dpool || !dkv || !dscore || !dape || !workspace)
+        return fail(SD_ERR_NULL_ARG, "compressor_pool_bwd: kv, score, ape, dpool, dkv, dscore, dape and workspace "
+                    "are required");
+    const void *ptrs[] = {kv, score, ape, dpool, dkv, dscore, dape, workspace};
+    int st = check_compressor("compressor_pool_bwd", B, S, D, ratio, overlap, dtype, ptrs, 8);
+    if (st != SD_OK) return st;
+    const size_t need = sd::compressor_bwd_workspace_bytes(B, S, D, ratio, overlap);
+    if (workspace_bytes < need)
+        return fail(SD_ERR_BAD_SHAPE, "compressor_pool_bwd: workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    return hip_status(sd::launch_compressor_pool_bwd(kv, score, ape, seg, dpool, B, S, D, ratio, overlap, dtype, dkv,
+                                                     dscore, dape, workspace, stream),
+                      "compressor_pool_bwd launch");
+}
+
 int distill_kl_fwd_bwd_noalloc(const float *target, const float *logits, const int32_t *idx, int B, int S, int K,
                                int N, float grad_scale, float *kl_rows, float *dlogits, float *stats,
                                hipStream_t stream) {

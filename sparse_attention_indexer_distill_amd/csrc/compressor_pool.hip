@@ -1,0 +1,388 @@
+// compressor_pool.hip -- the compressor that builds the compressed pool rows, on gfx950.
+//
+// Primus PR "Docker Build for DeepSeek-v4 (Don't Merge)", commit fusing the compressed-
+// attention small kernels: score + ape, a softmax over the window and the weighted sum in
+// one launch, with an analytic backward for kv, score and ape; HCA windows do not overlap,
+// CSA windows do.  Entry n pools the tokens j = r*n - OVL*r + i, i < Wc = r*(1+OVL), of its
+// batch row (positions before token 0, or whose token lies in another segment than the
+// entry's last token, are absent):
+//     w_i = softmax_i(score[j,d] + ape[i,d]) per channel d,   pool[n,d] = sum_i w_i kv[j,d]
+// Backward for dpool:
+//     dkv[j,d]    = sum over entries holding j of w dpool
+//     dscore[j,d] = sum over entries holding j of w (kv[j,d] - pool[n,d]) dpool
+//     dape[i,d]   = sum over b, n of the same product at position i
+//
+// The work is a stream over kv and score (HBM-bound; every token row is read by one or two
+// entries, the second time from L2).  Forward: one thread per (entry, CPT consecutive
+// channels), an online softmax in exp2 form over the window.  Backward: one thread per
+// (chunk of kChunk entries, CPT channels); for every window it recomputes the weights and
+// the pooled value, writes each block's dkv and dscore once (with overlap a block takes
+// contributions from two windows, so a chunk also recomputes the first window of the next
+// chunk), and accumulates dape for its own windows in registers.  The per-chunk dape
+// partials are added in a fixed order by a second kernel, so every result is bitwise
+// repeatable.
+#include "sd_device.hpp"
+#include "sd_internal.hpp"
+
+namespace sd {
+namespace {
+
+constexpr int kChunk = 8;        // entries per backward thread
+constexpr int kPoolThreads = 256;
+
+// CPT consecutive channels of one row (bf16 or fp32) as fp32.
+template <int DT, int CPT>
+__device__ __forceinline__ void load_ch(const void *base, int64_t elem, float (&o)[CPT]) {
+    if constexpr (DT == 0) {
+        const uint16_t *p = reinterpret_cast<const uint16_t *>(base) + elem;
+        if constexpr (CPT == 4) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(p);
+            o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+            o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+        } else if constexpr (CPT == 2) {
+            const uint32_t v = *reinterpret_cast<const uint32_t *>(p);
+            o[0] = __uint_as_float(v << 16); o[1] = __uint_as_float(v & 0xffff0000u);
+        } else {
+            o[0] = __uint_as_float((uint32_t)p[0] << 16);
+        }
+    } else {
+        const float *p = reinterpret_cast<const float *>(base) + elem;
+        if constexpr (CPT == 4) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+            o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
+        } else {
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) o[c] = p[c];
+        }
+    }
+}
+
+template <int CPT>
+__device__ __forceinline__ void load_f32(const float *p, float (&o)[CPT]) {
+    if constexpr (CPT == 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+        o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
+    } else {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) o[c] = p[c];
+    }
+}
+
+template <int CPT>
+__device__ __forceinline__ void store_f32(float *p, const float (&v)[CPT]) {
+    if constexpr (CPT == 4) {
+        *reinterpret_cast<f32x4 *>(p) = f32x4{v[0], v[1], v[2], v[3]};
+    } else {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) p[c] = v[c];
+    }
+}
+
+struct PoolArgs {
+    const void *kv, *score;
+    const float *ape;
+    const int32_t *seg;
+    const float *dpool;
+    float *pool, *dkv, *dscore, *dape_part, *dape;
+    int B, S, D, N, nchunk;
+};
+
+// Is position i of entry n present (token inside the row, same segment as the entry's last)?
+template <int R, int OVL>
+__device__ __forceinline__ bool present(const int32_t *sg, int n, int i, int32_t seg_last) {
+    const int j = R * n - OVL * R + i;
+    return j >= 0 && (sg == nullptr || sg[j] == seg_last);
+}
+
+template <int DT, int R, int OVL, int CPT>
+__global__ __launch_bounds__(kPoolThreads) void compressor_pool_kernel(const PoolArgs a) {
+    constexpr int Wc = R * (1 + OVL);
+    const int G = a.D / CPT;
+    const int64_t tid = (int64_t)blockIdx.x * kPoolThreads + threadIdx.x;
+    if (tid >= (int64_t)a.B * a.N * G) return;
+    const int g = (int)(tid % G);
+    const int64_t bn = tid / G;
+    const int n = (int)(bn % a.N);
+    const int64_t b = bn / a.N;
+    const int d0 = g * CPT;
+    const int32_t *sg = a.seg ? a.seg + b * a.S : nullptr;
+    const int32_t seg_last = sg ? sg[R * n + R - 1] : 0;
+    float m[CPT], den[CPT], num[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        m[c] = -INFINITY;
+        den[c] = 0.f;
+        num[c] = 0.f;
+    }
+#pragma unroll(Wc <= 16 ? Wc : 8)
+    for (int i = 0; i < Wc; ++i) {
+        if (!present<R, OVL>(sg, n, i, seg_last)) continue;
+        const int64_t row = b * a.S + (R * n - OVL * R + i);
+        float s[CPT], k[CPT], ap[CPT];
+        load_ch<DT, CPT>(a.score, row * a.D + d0, s);
+        load_ch<DT, CPT>(a.kv, row * a.D + d0, k);
+        load_f32<CPT>(a.ape + (int64_t)i * a.D + d0, ap);
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const float l = (s[c] + ap[c]) * kLog2e;
+            if (l > m[c]) {                       // new running maximum: rescale the sums
+                const float f = fast_exp2(m[c] - l);
+                den[c] *= f;
+                num[c] *= f;
+                m[c] = l;
+            }
+            const float e = fast_exp2(l - m[c]);
+            den[c] += e;
+            num[c] = fmaf(e, k[c], num[c]);
+        }
+    }
+    float out[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) out[c] = num[c] / den[c];   // the entry's last token is always present
+    store_f32<CPT>(a.pool + bn * a.D + d0, out);
+}
+
+// Weights of window n for CPT channels: the log2-domain maximum and the sum of exponentials.
+template <int DT, int R, int OVL, int CPT>
+__device__ __forceinline__ void window_stats(const PoolArgs &a, const int32_t *sg, int64_t b, int n, int d0,
+                                             int32_t seg_last, float (&m)[CPT], float (&den)[CPT],
+                                             float (&pool)[CPT]) {
+    constexpr int Wc = R * (1 + OVL);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        m[c] = -INFINITY;
+        den[c] = 0.f;
+        pool[c] = 0.f;
+    }
+#pragma unroll(Wc <= 16 ? Wc : 8)
+    for (int i = 0; i < Wc; ++i) {
+        if (!present<R, OVL>(sg, n, i, seg_last)) continue;
+        const int64_t row = b * a.S + (R * n - OVL * R + i);
+        float s[CPT], ap[CPT];
+        load_ch<DT, CPT>(a.score, row * a.D + d0, s);
+        load_f32<CPT>(a.ape + (int64_t)i * a.D + d0, ap);
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) m[c] = fmaxf(m[c], (s[c] + ap[c]) * kLog2e);
+    }
+#pragma unroll(Wc <= 16 ? Wc : 8)
+    for (int i = 0; i < Wc; ++i) {
+        if (!present<R, OVL>(sg, n, i, seg_last)) continue;
+        const int64_t row = b * a.S + (R * n - OVL * R + i);
+        float s[CPT], k[CPT], ap[CPT];
+        load_ch<DT, CPT>(a.score, row * a.D + d0, s);
+        load_ch<DT, CPT>(a.kv, row * a.D + d0, k);
+        load_f32<CPT>(a.ape + (int64_t)i * a.D + d0, ap);
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const float e = fast_exp2((s[c] + ap[c]) * kLog2e - m[c]);
+            den[c] += e;
+            pool[c] = fmaf(e, k[c], pool[c]);
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) pool[c] /= den[c];
+}
+
+template <int DT, int R, int OVL, int CPT>
+__global__ __launch_bounds__(kPoolThreads) void compressor_pool_bwd_kernel(const PoolArgs a) {
+    constexpr int Wc = R * (1 + OVL);
+    const int G = a.D / CPT;
+    const int64_t tid = (int64_t)blockIdx.x * kPoolThreads + threadIdx.x;
+    if (tid >= (int64_t)a.B * a.nchunk * G) return;
+    const int g = (int)(tid % G);
+    const int64_t bc = tid / G;
+    const int chunk = (int)(bc % a.nchunk);
+    const int64_t b = bc / a.nchunk;
+    const int d0 = g * CPT;
+    const int32_t *sg = a.seg ? a.seg + b * a.S : nullptr;
+    const int n0 = chunk * kChunk;
+    const int n_own_end = n0 + kChunk < a.N ? n0 + kChunk : a.N;   // windows [n0, n_own_end) are this thread's
+    // with overlap, block n_own_end - 1 also takes a contribution from window n_own_end
+    const int n_last = OVL && n_own_end < a.N ? n_own_end : n_own_end - 1;
+
+    float dape_acc[Wc][CPT];
+#pragma unroll
+    for (int i = 0; i < Wc; ++i)
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) dape_acc[i][c] = 0.f;
+    float carry_g[OVL ? R : 1][CPT], carry_h[OVL ? R : 1][CPT];  // block n's share from window n (overlap)
+
+    for (int n = n0; n <= n_last; ++n) {
+        const int32_t seg_last = sg ? sg[R * n + R - 1] : 0;
+        float m[CPT], den[CPT], pool[CPT], dp[CPT];
+        window_stats<DT, R, OVL, CPT>(a, sg, b, n, d0, seg_last, m, den, pool);
+        load_f32<CPT>(a.dpool + (b * a.N + n) * a.D + d0, dp);
+        const bool own = n < n_own_end;
+#pragma unroll(Wc <= 16 ? Wc : 8)
+        for (int i = 0; i < Wc; ++i) {
+            const int j = R * n - OVL * R + i;
+            float gv[CPT], hv[CPT];
+            if (present<R, OVL>(sg, n, i, seg_last)) {
+                const int64_t row = b * a.S + j;
+                float s[CPT], k[CPT], ap[CPT];
+                load_ch<DT, CPT>(a.score, row * a.D + d0, s);
+                load_ch<DT, CPT>(a.kv, row * a.D + d0, k);
+                load_f32<CPT>(a.ape + (int64_t)i * a.D + d0, ap);
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) {
+                    const float w = fast_exp2((s[c] + ap[c]) * kLog2e - m[c]) / den[c];
+                    gv[c] = w * dp[c];
+                    hv[c] = gv[c] * (k[c] - pool[c]);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) gv[c] = hv[c] = 0.f;
+            }
+            if (own) {
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) dape_acc[i][c] += hv[c];
+            }
+            if constexpr (OVL == 0) {
+                const int64_t o = (b * a.S + j) * a.D + d0;
+                store_f32<CPT>(a.dkv + o, gv);
+                store_f32<CPT>(a.dscore + o, hv);
+            } else if (i < R) {
+                // the previous block: complete it when this thread owns it (window n-1 was its first share)
+                if (n - 1 >= n0 && j >= 0) {
+                    float g2[CPT], h2[CPT];
+#pragma unroll
+                    for (int c = 0; c < CPT; ++c) {
+                        g2[c] = carry_g[i][c] + gv[c];
+                        h2[c] = carry_h[i][c] + hv[c];
+                    }
+                    const int64_t o = (b * a.S + j) * a.D + d0;
+                    store_f32<CPT>(a.dkv + o, g2);
+                    store_f32<CPT>(a.dscore + o, h2);
+                }
+            } else if (own) {
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) {
+                    carry_g[i - R][c] = gv[c];
+                    carry_h[i - R][c] = hv[c];
+                }
+            }
+        }
+    }
+    if constexpr (OVL == 1) {
+        if (n_own_end == a.N) {  // the last block has no later window
+            for (int i = 0; i < R; ++i) {
+                const int64_t o = (b * a.S + (int64_t)R * (a.N - 1) + i) * a.D + d0;
+                store_f32<CPT>(a.dkv + o, carry_g[i]);
+                store_f32<CPT>(a.dscore + o, carry_h[i]);
+            }
+        }
+    }
+    if (n_own_end == a.N) {      // tokens past the last entry are in no window
+        float z[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) z[c] = 0.f;
+        for (int j = R * a.N; j < a.S; ++j) {
+            const int64_t o = (b * a.S + j) * a.D + d0;
+            store_f32<CPT>(a.dkv + o, z);
+            store_f32<CPT>(a.dscore + o, z);
+        }
+    }
+    float *part = a.dape_part + (b * a.nchunk + chunk) * (int64_t)Wc * a.D + d0;
+#pragma unroll
+    for (int i = 0; i < Wc; ++i) store_f32<CPT>(part + (int64_t)i * a.D, dape_acc[i]);
+}
+
+// dape[i,d] = sum over the B*nchunk partials in order.
+__global__ __launch_bounds__(kPoolThreads) void compressor_dape_kernel(const float *__restrict__ part, int nparts,
+                                                                       int64_t WcD, float *__restrict__ dape) {
+    const int64_t x = (int64_t)blockIdx.x * kPoolThreads + threadIdx.x;
+    if (x >= WcD) return;
+    float s = 0.f;
+    for (int p = 0; p < nparts; ++p) s += part[(int64_t)p * WcD + x];
+    dape[x] = s;
+}
+
+template <int R, int OVL>
+constexpr int cpt_for() {
+    return R * (1 + OVL) <= 8 ? 4 : (R * (1 + OVL) <= 32 ? 2 : 1);
+}
+
+template <int DT, int R, int OVL>
+hipError_t launch_fwd(const PoolArgs &a, hipStream_t stream) {
+    constexpr int CPT = cpt_for<R, OVL>();
+    const int64_t threads = (int64_t)a.B * a.N * (a.D / CPT);
+    hipLaunchKernelGGL((compressor_pool_kernel<DT, R, OVL, CPT>), dim3((unsigned)((threads + kPoolThreads - 1) / kPoolThreads)),
+                       dim3(kPoolThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int DT, int R, int OVL>
+hipError_t launch_bwd(const PoolArgs &a, hipStream_t stream) {
+    constexpr int CPT = cpt_for<R, OVL>();
+    constexpr int Wc = R * (1 + OVL);
+    const int64_t threads = (int64_t)a.B * a.nchunk * (a.D / CPT);
+    hipLaunchKernelGGL((compressor_pool_bwd_kernel<DT, R, OVL, CPT>),
+                       dim3((unsigned)((threads + kPoolThreads - 1) / kPoolThreads)), dim3(kPoolThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t WcD = (int64_t)Wc * a.D;
+    hipLaunchKernelGGL(compressor_dape_kernel, dim3((unsigned)((WcD + kPoolThreads - 1) / kPoolThreads)),
+                       dim3(kPoolThreads), 0, stream, a.dape_part, a.B * a.nchunk, WcD, a.dape);
+    return hipGetLastError();
+}
+
+template <int DT, bool BWD>
+hipError_t dispatch(const PoolArgs &a, int ratio, int overlap, hipStream_t stream) {
+#define SD_CP(R, O) return BWD ? launch_bwd<DT, R, O>(a, stream) : launch_fwd<DT, R, O>(a, stream)
+    if (overlap) {
+        switch (ratio) {
+            case 1: SD_CP(1, 1);
+            case 2: SD_CP(2, 1);
+            case 4: SD_CP(4, 1);
+            case 8: SD_CP(8, 1);
+            case 16: SD_CP(16, 1);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    switch (ratio) {
+        case 1: SD_CP(1, 0);
+        case 2: SD_CP(2, 0);
+        case 4: SD_CP(4, 0);
+        case 8: SD_CP(8, 0);
+        case 16: SD_CP(16, 0);
+        case 32: SD_CP(32, 0);
+        case 64: SD_CP(64, 0);
+        case 128: SD_CP(128, 0);
+        default: return hipErrorInvalidValue;
+    }
+#undef SD_CP
+}
+
+}  // namespace
+
+bool compressor_supported(int ratio, int overlap) {
+    const bool pow2 = ratio > 0 && (ratio & (ratio - 1)) == 0;
+    return pow2 && (overlap ? ratio <= 16 : ratio <= 128);
+}
+
+size_t compressor_bwd_workspace_bytes(int B, int S, int D, int ratio, int overlap) {
+    const int64_t N = S / ratio;
+    const int64_t nchunk = (N + kChunk - 1) / kChunk;
+    return (size_t)((int64_t)B * nchunk * ratio * (1 + overlap) * D * (int64_t)sizeof(float));
+}
+
+hipError_t launch_compressor_pool(const void *kv, const void *score, const float *ape, const int32_t *seg, int B,
+                                  int S, int D, int ratio, int overlap, int dtype, float *pool, hipStream_t stream) {
+    PoolArgs a{};
+    a.kv = kv; a.score = score; a.ape = ape; a.seg = seg; a.pool = pool;
+    a.B = B; a.S = S; a.D = D; a.N = S / ratio;
+    return dtype == 0 ? dispatch<0, false>(a, ratio, overlap, stream) : dispatch<1, false>(a, ratio, overlap, stream);
+}
+
+hipError_t launch_compressor_pool_bwd(const void *kv, const void *score, const float *ape, const int32_t *seg,
+                                      const float *dpool, int B, int S, int D, int ratio, int overlap, int dtype,
+                                      float *dkv, float *dscore, float *dape, void *workspace, hipStream_t stream) {
+    PoolArgs a{};
+    a.kv = kv; a.score = score; a.ape = ape; a.seg = seg; a.dpool = dpool;
+    a.dkv = dkv; a.dscore = dscore; a.dape = dape; a.dape_part = reinterpret_cast<float *>(workspace);
+    a.B = B; a.S = S; a.D = D; a.N = S / ratio;
+    a.nchunk = (a.N + kChunk - 1) / kChunk;
+    return dtype == 0 ? dispatch<0, true>(a, ratio, overlap, stream) : dispatch<1, true>(a, ratio, overlap, stream);
+}
+
+}  // namespace sd

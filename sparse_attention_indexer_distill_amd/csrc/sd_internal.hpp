@@ -68,4 +68,12 @@ hipError_t launch_indexer_topk(const float *scores, const int32_t *seg, int B, i
 hipError_t launch_indexer_topk_bwd(const float *dvalues, const int32_t *idx, int B, int S, int N, int K,
                                    float *dscores, hipStream_t stream);
 
+bool compressor_supported(int ratio, int overlap);
+size_t compressor_bwd_workspace_bytes(int B, int S, int D, int ratio, int overlap);
+hipError_t launch_compressor_pool(const void *kv, const void *score, const float *ape, const int32_t *seg, int B,
+                                  int S, int D, int ratio, int overlap, int dtype, float *pool, hipStream_t stream);
+hipError_t launch_compressor_pool_bwd(const void *kv, const void *score, const float *ape, const int32_t *seg,
+                                      const float *dpool, int B, int S, int D, int ratio, int overlap, int dtype,
+                                      float *dkv, float *dscore, float *dape, void *workspace, hipStream_t stream);
+
 }  // namespace sd

@@ -161,6 +161,24 @@ def student_scores(cfg: Config | str, ties: bool = False) -> torch.Tensor:
     return torch.from_numpy(s)
 
 
+def compressor_inputs(cfg: Config | str, ratio: int, overlap: bool, dtype: Optional[str] = None) -> dict:
+    """Inputs of the compressor at a workload's shape: kv and score [B,S,D] (N(0,1), rounded to
+    bf16 for bf16 workloads), ape [Wc,D] fp32 (N(0,1)/2), the upstream gradient dpool
+    [B,S//ratio,D] fp32 (N(0,1)), and the workload's segment ids."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    dt = cfg.dtype if dtype is None else dtype
+    B, S, D = cfg.B, cfg.S, cfg.D
+    Wc = ratio * (2 if overlap else 1)
+    kv = _normal(rng_for(cfg, "kv"), (B, S, D))
+    score = _normal(rng_for(cfg, "cscore"), (B, S, D))
+    ape = 0.5 * _normal(rng_for(cfg, "ape"), (Wc, D))
+    dpool = _normal(rng_for(cfg, "dout"), (B, S // ratio, D))
+    seg = segment_ids(cfg)
+    return dict(kv=_round(kv, dt), score=_round(score, dt), ape=torch.from_numpy(ape.astype(np.float32)),
+                dpool=torch.from_numpy(dpool), seg=None if seg is None else torch.from_numpy(seg))
+
+
 def make_inputs(cfg: Config | str, shuffle_pad: bool = False) -> dict:
     """Draw every input of one workload.  Returns host tensors:
 

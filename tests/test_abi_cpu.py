@@ -35,6 +35,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("window_lse", "distill_target", "distill_target_fused", "distill_kl_fwd_bwd",
               "distill_kl_workspace_bytes", "distill_kl_fwd_bwd_noalloc", "indexer_topk", "indexer_topk_bwd",
+              "compressor_pool", "compressor_pool_bwd", "compressor_pool_bwd_workspace_bytes",
               "sd_status_string", "sd_last_error"):
         assert n in names, names
 
@@ -200,6 +201,35 @@ def test_indexer_topk_rejections(lib):
     assert bwd(out=None) == sd.SD_ERR_NULL_ARG
     assert bwd(S=0) == sd.SD_ERR_BAD_SHAPE
     assert bwd(N=5000) == sd.SD_ERR_UNSUPPORTED
+
+
+def test_compressor_rejections(lib):
+    A = ctypes.c_void_p(0x1000)       # 16-byte aligned placeholder
+
+    def fwd(kv=A, sc=A, ape=A, out=A, B=1, S=16, D=8, r=4, ovl=1, dt=0):
+        return lib.compressor_pool(kv, sc, ape, None, B, S, D, r, ovl, dt, out, None)
+
+    def bwd(ws=A, wsb=1 << 20, D=8, r=4, ovl=1, dp=A):
+        return lib.compressor_pool_bwd(A, A, A, None, dp, 1, 16, D, r, ovl, 0, A, A, A, ws, wsb, None)
+    assert fwd(kv=None) == sd.SD_ERR_NULL_ARG
+    assert fwd(out=None) == sd.SD_ERR_NULL_ARG
+    assert fwd(dt=3) == sd.SD_ERR_DTYPE
+    assert fwd(S=3) == sd.SD_ERR_BAD_SHAPE            # no complete block
+    assert fwd(ovl=2) == sd.SD_ERR_BAD_SHAPE
+    assert fwd(D=6) == sd.SD_ERR_UNSUPPORTED
+    assert fwd(r=3) == sd.SD_ERR_UNSUPPORTED          # not a power of two
+    assert fwd(r=32, S=64) == sd.SD_ERR_UNSUPPORTED   # overlap covers ratios up to 16
+    assert fwd(r=256, S=512, ovl=0) == sd.SD_ERR_UNSUPPORTED
+    assert fwd(kv=ctypes.c_void_p(0x1008)) == sd.SD_ERR_BAD_SHAPE   # not 16-byte aligned
+    assert b"aligned" in lib.sd_last_error()
+    # workspace: (B * ceil(N / 8)) chunks x Wc x D floats
+    assert lib.compressor_pool_bwd_workspace_bytes(1, 16, 8, 4, 1) == 1 * 1 * 8 * 8 * 4
+    assert lib.compressor_pool_bwd_workspace_bytes(2, 1000, 8, 4, 0) == 2 * 32 * 4 * 8 * 4
+    assert lib.compressor_pool_bwd_workspace_bytes(1, 3, 8, 4, 0) == 0
+    assert bwd(ws=None) == sd.SD_ERR_NULL_ARG
+    assert bwd(dp=None) == sd.SD_ERR_NULL_ARG
+    assert bwd(wsb=8) == sd.SD_ERR_BAD_SHAPE
+    assert b"workspace" in lib.sd_last_error()
 
 
 def test_binding_rejects_host_tensors():

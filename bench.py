@@ -147,6 +147,78 @@ def cpu_baseline(cfg, x, ms_per_step: float) -> dict:
             "cpu": cpu, "nproc": os.cpu_count(), "gpu_speedup": round(ms_layer / ms_per_step, 1)}
 
 
+def time_launches(fn, steps: int, warmup: int, reps: int = 20) -> dict:
+    """Mean/median/min per-launch duration of fn() (kernel launches only, on torch's current
+    stream).  The launches are captured as one HIP graph of `reps` back-to-back calls and the
+    graph is replayed between HIP events, so the host's per-call overhead (longer than these
+    small kernels) never leaves the GPU idle inside the timed interval."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        graph.replay()
+        b.record()
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) / reps for a, b in evs]
+    return {"ms": float(np.mean(t)), "ms_median": float(np.median(t)), "ms_min": float(np.min(t))}
+
+
+def next_rows(cfg, sd, dev, steps: int, warmup: int) -> dict:
+    """The steps next to the layer, at the workload's shape, each against its HBM roofline:
+    the indexer's masked top-k (scores [B,S,N] -> idx, values) and its gradient scatter, and the
+    CSA compressor (ratio 4, overlapping windows, kv/score [B,S,D] bf16 -> pool [B,N,D]) with its
+    backward.  Algorithmic bytes: the visible part of the scores row (the blocks complete at t)
+    plus the outputs; the scatter's inputs plus its dense [B,S,N] output; the compressor's kv and
+    score once plus pool (and, backward, dpool plus dkv and dscore)."""
+    B, S, N, K, D = cfg.B, cfg.S, cfg.N, cfg.K, cfg.D
+    out = {}
+    scores = synth.student_scores(cfg).to(dev)
+    seg = synth.segment_ids(cfg)
+    seg = None if seg is None else torch.from_numpy(seg).to(dev)
+    idx = torch.empty(B, S, K, dtype=torch.int32, device=dev)
+    val = torch.empty(B, S, K, device=dev)
+    t = np.arange(S)
+    vis = int(B * np.minimum(N, (t + 1) // 4).sum())
+    r = time_launches(lambda: sd.indexer_topk(scores, seg, K=K, ratio=4, out_idx=idx, out_values=val), steps, warmup)
+    r["algorithmic_bytes"] = vis * 4 + B * S * K * 8
+    out["indexer_topk"] = r
+    dv = torch.randn(B, S, K, device=dev)
+    dsc = torch.empty(B, S, N, device=dev)
+    r = time_launches(lambda: sd.indexer_topk_bwd(dv, idx, N, out=dsc), steps, warmup)
+    r["algorithmic_bytes"] = B * S * K * 8 + B * S * N * 4
+    out["indexer_topk_bwd"] = r
+    x = synth.compressor_inputs(cfg, 4, True)
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    pool = torch.empty(B, S // 4, D, device=dev)
+    r = time_launches(lambda: sd.compressor_pool(g["kv"], g["score"], g["ape"], g["seg"], ratio=4, overlap=True,
+                                                 out=pool), steps, warmup)
+    e = g["kv"].element_size()
+    r["algorithmic_bytes"] = 2 * B * S * D * e + 8 * D * 4 + B * (S // 4) * D * 4
+    out["compressor_pool"] = r
+    dkv = torch.empty(B, S, D, device=dev)
+    dsco = torch.empty(B, S, D, device=dev)
+    dape = torch.empty(8, D, device=dev)
+    ws = torch.empty(max(16, sd.compressor_pool_bwd_workspace_bytes(B, S, D, 4, True)), dtype=torch.uint8, device=dev)
+    r = time_launches(lambda: sd.compressor_pool_bwd(g["kv"], g["score"], g["ape"], g["dpool"], g["seg"], ratio=4,
+                                                     overlap=True, dkv=dkv, dscore=dsco, dape=dape, workspace=ws),
+                      steps, warmup)
+    r["algorithmic_bytes"] = 2 * B * S * D * e + B * (S // 4) * D * 4 + 2 * B * S * D * 4 + 16 * D * 4
+    out["compressor_pool_bwd"] = r
+    for v in out.values():
+        gbs = v["algorithmic_bytes"] / (v["ms"] * 1e-3) / 1e9
+        v.update({"GB/s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "bound": "hbm",
+                  "ms": round(v["ms"], 4), "ms_median": round(v["ms_median"], 4), "ms_min": round(v["ms_min"], 4)})
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,6 +230,8 @@ def main() -> int:
     ap.add_argument("--path", default="fused", choices=["3call", "fused"],
                     help="3call: window_lse -> distill_target -> KL; fused: distill_target_fused -> KL")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip timing the indexer top-k and compressor steps next to the layer")
     ap.add_argument("--graph", action="store_true",
                     help="time whole steps as replays of one captured HIP graph of the step")
     ap.add_argument("--l2-cold", action="store_true",
@@ -301,6 +375,8 @@ def main() -> int:
         **({"l2_cold_ms_median": cold} if cold is not None else {}),
         "layer_useful_TFLOP/s": round(sum(work[n]["flops"] for n in names) / (ms_per_step * 1e-3) / 1e12, 1),
     }
+    if not args.no_next_rows:
+        out["next_rows"] = next_rows(cfg, sd, dev, max(args.steps, 20), min(max(args.warmup, 5), 50))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, x, ms_per_step)
     print(json.dumps(out), flush=True)

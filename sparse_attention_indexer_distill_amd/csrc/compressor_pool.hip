@@ -15,20 +15,22 @@
 // The work is a stream over kv and score (HBM-bound; every token row is read by one or two
 // entries, the second time from L2).  Forward: one thread per (entry, CPT consecutive
 // channels), an online softmax in exp2 form over the window.  Backward: one thread per
-// (chunk of kChunk entries, CPT channels); for every window it recomputes the weights and
-// the pooled value, writes each block's dkv and dscore once (with overlap a block takes
+// (chunk of kChunk entries, CPT channels), 64 channel groups to a wave and four consecutive
+// chunks to a workgroup; for every window it recomputes the weights and the pooled value in
+// one online pass, then writes each block's dkv and dscore once (with overlap a block takes
 // contributions from two windows, so a chunk also recomputes the first window of the next
-// chunk), and accumulates dape for its own windows in registers.  The per-chunk dape
-// partials are added in a fixed order by a second kernel, so every result is bitwise
-// repeatable.
+// chunk) and accumulates dape for its own windows in registers.  The workgroup's four waves
+// add their dape in LDS in a fixed order, and a second kernel adds the per-workgroup
+// partials in a fixed order, so every result is bitwise repeatable.
 #include "sd_device.hpp"
 #include "sd_internal.hpp"
 
 namespace sd {
 namespace {
 
-constexpr int kChunk = 8;        // entries per backward thread
+constexpr int kChunk = 2;        // entries per backward thread
 constexpr int kPoolThreads = 256;
+constexpr int kBwdWaves = 4;     // chunks per backward workgroup, one wave each
 
 // CPT consecutive channels of one row (bf16 or fp32) as fp32.
 template <int DT, int CPT>
@@ -84,7 +86,7 @@ struct PoolArgs {
     const int32_t *seg;
     const float *dpool;
     float *pool, *dkv, *dscore, *dape_part, *dape;
-    int B, S, D, N, nchunk;
+    int B, S, D, N, nchunk, ncb;  // ncb: workgroups of kBwdWaves chunks per batch row
 };
 
 // Is position i of entry n present (token inside the row, same segment as the entry's last)?
@@ -142,7 +144,8 @@ __global__ __launch_bounds__(kPoolThreads) void compressor_pool_kernel(const Poo
     store_f32<CPT>(a.pool + bn * a.D + d0, out);
 }
 
-// Weights of window n for CPT channels: the log2-domain maximum and the sum of exponentials.
+// Statistics of window n for CPT channels in one online pass: the log2-domain maximum m, the
+// sum of exponentials den and the pooled value.
 template <int DT, int R, int OVL, int CPT>
 __device__ __forceinline__ void window_stats(const PoolArgs &a, const int32_t *sg, int64_t b, int n, int d0,
                                              int32_t seg_last, float (&m)[CPT], float (&den)[CPT],
@@ -158,23 +161,20 @@ __device__ __forceinline__ void window_stats(const PoolArgs &a, const int32_t *s
     for (int i = 0; i < Wc; ++i) {
         if (!present<R, OVL>(sg, n, i, seg_last)) continue;
         const int64_t row = b * a.S + (R * n - OVL * R + i);
-        float s[CPT], ap[CPT];
-        load_ch<DT, CPT>(a.score, row * a.D + d0, s);
-        load_f32<CPT>(a.ape + (int64_t)i * a.D + d0, ap);
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) m[c] = fmaxf(m[c], (s[c] + ap[c]) * kLog2e);
-    }
-#pragma unroll(Wc <= 16 ? Wc : 8)
-    for (int i = 0; i < Wc; ++i) {
-        if (!present<R, OVL>(sg, n, i, seg_last)) continue;
-        const int64_t row = b * a.S + (R * n - OVL * R + i);
         float s[CPT], k[CPT], ap[CPT];
         load_ch<DT, CPT>(a.score, row * a.D + d0, s);
         load_ch<DT, CPT>(a.kv, row * a.D + d0, k);
         load_f32<CPT>(a.ape + (int64_t)i * a.D + d0, ap);
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
-            const float e = fast_exp2((s[c] + ap[c]) * kLog2e - m[c]);
+            const float l = (s[c] + ap[c]) * kLog2e;
+            if (l > m[c]) {
+                const float f = fast_exp2(m[c] - l);
+                den[c] *= f;
+                pool[c] *= f;
+                m[c] = l;
+            }
+            const float e = fast_exp2(l - m[c]);
             den[c] += e;
             pool[c] = fmaf(e, k[c], pool[c]);
         }
@@ -183,22 +183,25 @@ __device__ __forceinline__ void window_stats(const PoolArgs &a, const int32_t *s
     for (int c = 0; c < CPT; ++c) pool[c] /= den[c];
 }
 
+// grid: (ceil(G / 64), B * ncb); lane -> channel group, wave -> chunk
 template <int DT, int R, int OVL, int CPT>
-__global__ __launch_bounds__(kPoolThreads) void compressor_pool_bwd_kernel(const PoolArgs a) {
+__global__ __launch_bounds__(kBwdWaves * 64) void compressor_pool_bwd_kernel(const PoolArgs a) {
     constexpr int Wc = R * (1 + OVL);
+    constexpr int SL = Wc * CPT <= 32 ? Wc : (32 / CPT);   // positions per LDS reduction slice
+    __shared__ float red[kBwdWaves][SL][64 * CPT];
     const int G = a.D / CPT;
-    const int64_t tid = (int64_t)blockIdx.x * kPoolThreads + threadIdx.x;
-    if (tid >= (int64_t)a.B * a.nchunk * G) return;
-    const int g = (int)(tid % G);
-    const int64_t bc = tid / G;
-    const int chunk = (int)(bc % a.nchunk);
-    const int64_t b = bc / a.nchunk;
-    const int d0 = g * CPT;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int g = blockIdx.x * 64 + lane;
+    const int64_t b = blockIdx.y / a.ncb;
+    const int cb = (int)(blockIdx.y - b * a.ncb);
+    const int chunk = cb * kBwdWaves + w;
+    const bool active = g < G && chunk < a.nchunk;   // inactive lanes still meet the barriers below
+    const int d0 = (g < G ? g : 0) * CPT;
     const int32_t *sg = a.seg ? a.seg + b * a.S : nullptr;
     const int n0 = chunk * kChunk;
-    const int n_own_end = n0 + kChunk < a.N ? n0 + kChunk : a.N;   // windows [n0, n_own_end) are this thread's
+    const int n_own_end = !active ? n0 : (n0 + kChunk < a.N ? n0 + kChunk : a.N);   // windows [n0, n_own_end)
     // with overlap, block n_own_end - 1 also takes a contribution from window n_own_end
-    const int n_last = OVL && n_own_end < a.N ? n_own_end : n_own_end - 1;
+    const int n_last = !active ? n0 - 1 : (OVL && n_own_end < a.N ? n_own_end : n_own_end - 1);
 
     float dape_acc[Wc][CPT];
 #pragma unroll
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(kPoolThreads) void compressor_pool_bwd_kernel(const
         }
     }
     if constexpr (OVL == 1) {
-        if (n_own_end == a.N) {  // the last block has no later window
+        if (active && n_own_end == a.N) {  // the last block has no later window
             for (int i = 0; i < R; ++i) {
                 const int64_t o = (b * a.S + (int64_t)R * (a.N - 1) + i) * a.D + d0;
                 store_f32<CPT>(a.dkv + o, carry_g[i]);
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(kPoolThreads) void compressor_pool_bwd_kernel(const
             }
         }
     }
-    if (n_own_end == a.N) {      // tokens past the last entry are in no window
+    if (active && n_own_end == a.N) {      // tokens past the last entry are in no window
         float z[CPT];
 #pragma unroll
         for (int c = 0; c < CPT; ++c) z[c] = 0.f;
@@ -282,24 +285,47 @@ __global__ __launch_bounds__(kPoolThreads) void compressor_pool_bwd_kernel(const
             store_f32<CPT>(a.dscore + o, z);
         }
     }
-    float *part = a.dape_part + (b * a.nchunk + chunk) * (int64_t)Wc * a.D + d0;
+    // the workgroup's dape: its four waves (chunks) added in order, one slice of positions at a time
+    float *part = a.dape_part + (int64_t)blockIdx.y * Wc * a.D;
 #pragma unroll
-    for (int i = 0; i < Wc; ++i) store_f32<CPT>(part + (int64_t)i * a.D, dape_acc[i]);
+    for (int i0 = 0; i0 < Wc; i0 += SL) {
+#pragma unroll
+        for (int ii = 0; ii < SL; ++ii)
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) red[w][ii][lane * CPT + c] = dape_acc[i0 + ii][c];
+        __syncthreads();
+        for (int e = threadIdx.x; e < SL * 64 * CPT; e += kBwdWaves * 64) {
+            const int ii = e / (64 * CPT), x = e - ii * (64 * CPT);
+            const int d = blockIdx.x * 64 * CPT + x;
+            if (d < a.D) {
+                float v = red[0][ii][x];
+#pragma unroll
+                for (int u = 1; u < kBwdWaves; ++u) v += red[u][ii][x];
+                part[(int64_t)(i0 + ii) * a.D + d] = v;
+            }
+        }
+        __syncthreads();
+    }
 }
 
-// dape[i,d] = sum over the B*nchunk partials in order.
-__global__ __launch_bounds__(kPoolThreads) void compressor_dape_kernel(const float *__restrict__ part, int nparts,
-                                                                       int64_t WcD, float *__restrict__ dape) {
-    const int64_t x = (int64_t)blockIdx.x * kPoolThreads + threadIdx.x;
-    if (x >= WcD) return;
+// dape[x] = sum over the per-workgroup partials: wave u adds partials u, u+4, ... in order,
+// then the four wave sums are added in order (64 entries x per workgroup).
+__global__ __launch_bounds__(256) void compressor_dape_kernel(const float *__restrict__ part, int nparts,
+                                                              int64_t WcD, float *__restrict__ dape) {
+    __shared__ float red[4][64];
+    const int lane = threadIdx.x & 63, u = threadIdx.x >> 6;
+    const int64_t x = (int64_t)blockIdx.x * 64 + lane;
     float s = 0.f;
-    for (int p = 0; p < nparts; ++p) s += part[(int64_t)p * WcD + x];
-    dape[x] = s;
+    if (x < WcD)
+        for (int p = u; p < nparts; p += 4) s += part[(int64_t)p * WcD + x];
+    red[u][lane] = s;
+    __syncthreads();
+    if (u == 0 && x < WcD) dape[x] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
 }
 
 template <int R, int OVL>
 constexpr int cpt_for() {
-    return R * (1 + OVL) <= 8 ? 4 : (R * (1 + OVL) <= 32 ? 2 : 1);
+    return R * (1 + OVL) <= 2 ? 4 : (R * (1 + OVL) <= 16 ? 2 : 1);
 }
 
 template <int DT, int R, int OVL>
@@ -315,14 +341,14 @@ template <int DT, int R, int OVL>
 hipError_t launch_bwd(const PoolArgs &a, hipStream_t stream) {
     constexpr int CPT = cpt_for<R, OVL>();
     constexpr int Wc = R * (1 + OVL);
-    const int64_t threads = (int64_t)a.B * a.nchunk * (a.D / CPT);
-    hipLaunchKernelGGL((compressor_pool_bwd_kernel<DT, R, OVL, CPT>),
-                       dim3((unsigned)((threads + kPoolThreads - 1) / kPoolThreads)), dim3(kPoolThreads), 0, stream, a);
+    const int G = a.D / CPT;
+    const dim3 grid((unsigned)((G + 63) / 64), (unsigned)((int64_t)a.B * a.ncb));
+    hipLaunchKernelGGL((compressor_pool_bwd_kernel<DT, R, OVL, CPT>), grid, dim3(kBwdWaves * 64), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t WcD = (int64_t)Wc * a.D;
-    hipLaunchKernelGGL(compressor_dape_kernel, dim3((unsigned)((WcD + kPoolThreads - 1) / kPoolThreads)),
-                       dim3(kPoolThreads), 0, stream, a.dape_part, a.B * a.nchunk, WcD, a.dape);
+    hipLaunchKernelGGL(compressor_dape_kernel, dim3((unsigned)((WcD + 63) / 64)), dim3(256), 0, stream, a.dape_part,
+                       a.B * a.ncb, WcD, a.dape);
     return hipGetLastError();
 }
 
@@ -363,7 +389,8 @@ bool compressor_supported(int ratio, int overlap) {
 size_t compressor_bwd_workspace_bytes(int B, int S, int D, int ratio, int overlap) {
     const int64_t N = S / ratio;
     const int64_t nchunk = (N + kChunk - 1) / kChunk;
-    return (size_t)((int64_t)B * nchunk * ratio * (1 + overlap) * D * (int64_t)sizeof(float));
+    const int64_t ncb = (nchunk + kBwdWaves - 1) / kBwdWaves;
+    return (size_t)((int64_t)B * ncb * ratio * (1 + overlap) * D * (int64_t)sizeof(float));
 }
 
 hipError_t launch_compressor_pool(const void *kv, const void *score, const float *ape, const int32_t *seg, int B,
@@ -382,6 +409,7 @@ hipError_t launch_compressor_pool_bwd(const void *kv, const void *score, const f
     a.dkv = dkv; a.dscore = dscore; a.dape = dape; a.dape_part = reinterpret_cast<float *>(workspace);
     a.B = B; a.S = S; a.D = D; a.N = S / ratio;
     a.nchunk = (a.N + kChunk - 1) / kChunk;
+    a.ncb = (a.nchunk + kBwdWaves - 1) / kBwdWaves;
     return dtype == 0 ? dispatch<0, true>(a, ratio, overlap, stream) : dispatch<1, true>(a, ratio, overlap, stream);
 }
 

@@ -12,8 +12,8 @@
 // Mapping: one wave per (b,t) row, element n of the row on lane n % 64, register n / 64,
 // so every load and every ordered prefix runs over 64 consecutive blocks.  Scores map to
 // order-preserving 32-bit keys (NaN -> 0, the smallest); the K-th largest visible key is
-// found most-significant bit first, one wave-wide count per bit (a compare per element,
-// then ballot population counts on the scalar unit), so no sort and no LDS are needed.
+// found most-significant bit first, one wave-wide count per bit (a compare and an add per
+// element on the vector unit, then one cross-lane sum), so no sort and no LDS are needed.
 // The backward is the adjoint of the gather values[k] = scores[idx[k]]: a dense row of N
 // gradients, built in LDS and streamed out with 16-byte stores.
 #include <math.h>
@@ -92,10 +92,11 @@ __global__ __launch_bounds__(kTopkWaves * 64) void indexer_topk_kernel(
     if (count > K) {
         for (int bit = 31; bit >= 0; --bit) {
             const uint32_t cand = tau | (1u << bit);
-            int cnt = 0;
+            // per-lane counts on the vector unit, then one wave sum (exact in fp32: <= 4096)
+            int c = 0;
 #pragma unroll
-            for (int e = 0; e < E; ++e) cnt += wave_popc(key[e] >= cand);
-            if (cnt >= K) tau = cand;
+            for (int e = 0; e < E; ++e) c += key[e] >= cand ? 1 : 0;
+            if (wave_sum((float)c) >= (float)K) tau = cand;
         }
         int greater = 0;
 #pragma unroll

@@ -38,6 +38,11 @@ def test_bench_prints_one_complete_json_line(monkeypatch, capsys):
     # the compulsory bytes
     assert r["traffic"] is None or r["traffic"] >= 0.95 * kt["algorithmic_bytes"]
 
+    nr = d["next_rows"]
+    assert set(nr) == {"indexer_topk", "indexer_topk_bwd", "compressor_pool", "compressor_pool_bwd"}
+    for v in nr.values():
+        assert v["ms"] > 0 and v["bound"] == "hbm" and 0 < v["hbm_frac"] < 1.5
+
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["unit"] == "ms" and c["value"] > 0 and c["cores"] >= 1
     assert isinstance(c["sample"], str) and "rows" in c["sample"]

@@ -14,7 +14,7 @@
 // a list in LDS; 16-slot tiles of that list are dealt round-robin to the waves, so invalid
 // (-1) slots cost no MFMA work wherever they sit.  Each wave gathers its rows from L2 in
 // 128-byte pieces (8 consecutive lanes on a row, the layout the memory pipeline merges),
-// regroups them into MFMA operand fragments with one ds_bpermute per dword, and
+// regroups them into MFMA operand fragments with one select and one ds_bpermute per dword, and
 // accumulates
 //     C[slot][head] (16x16 tiles) = pool_row . q_head
 // for all heads, keeping every score of its slots in registers.  The epilogue has one
@@ -179,17 +179,23 @@ __device__ __forceinline__ void score_dispatch_f32(int my, f32x4 (&acc)[KT][HT],
 
 // bf16 scores from 128-byte row pieces (two chunks per load pair; see pair_frags).  The
 // tiles are scored PT at a time, so only PT tiles' raw loads and fragments are live next
-// to the accumulators; the next piece's loads are issued as soon as the current one has
-// been permuted, and each query fragment is read from LDS once per chunk and pass.  With
-// an odd chunk count the last piece is half used (its upper 64 bytes belong to the next
-// row, or fall past the buffer end and read as zero).  cr rotates the piece order per
-// wave and token, which spreads the gathers over the L2 channels.
-template <int HT, int MY, int KT, int PT>
+// to the accumulators; the loads of piece p + DEPTH are issued as soon as piece p has been
+// permuted (DEPTH pieces in flight, in a ring of raw registers), and each query fragment is
+// read from LDS once per chunk and pass.  With an odd chunk count the last piece is half
+// used (its upper 64 bytes belong to the next row, or fall past the buffer end and read as
+// zero).  cr rotates the piece order per wave and token, which spreads the gathers over the
+// L2 channels.
+// SOFF (even chunk counts only): the piece offset goes in the load's scalar offset.  Every
+// access of a load then lies inside one pool row; with an odd chunk count the half-used last
+// piece reaches past the row, and those loads keep the whole offset in the vector operand,
+// which the buffer's range check covers (reads past the pool's end return zero).
+template <int HT, int MY, int KT, int PT, bool SOFF, int DEPTH>
 __device__ __forceinline__ void score_pairs(f32x4 (&acc)[KT][HT], const unsigned char *__restrict__ qb,
                                             rsrc_t pool, const uint32_t (&olo)[KT], const uint32_t (&ohi)[KT],
                                             int nch, int cr, int lane) {
     const int np = (nch + 1) >> 1;
     const PairAddr pa = pair_frag_addr(lane);
+    const bool lo_first = (lane & 4) == 0;  // this lane's chunk-2p dword is in lo (else in hi)
     const unsigned char *qlane0 = qb + q_lane_bytes(lane, 0), *qlane1 = qb + q_lane_bytes(lane, 1);
     auto rot = [&](int p) {
         const int pp = p + cr;
@@ -197,25 +203,29 @@ __device__ __forceinline__ void score_pairs(f32x4 (&acc)[KT][HT], const unsigned
     };
 #pragma unroll
     for (int l0 = 0; l0 < MY; l0 += PT) {
-        u32x4 lo[PT], hi[PT];
-        auto load = [&](int p) {
-            const uint32_t pb = (uint32_t)rot(p) * 128u;
+        u32x4 lo[DEPTH][PT], hi[DEPTH][PT];
+        auto load = [&](u32x4(&l)[PT], u32x4(&h)[PT], int p) {
+            const uint32_t pb = (uint32_t)__builtin_amdgcn_readfirstlane(rot(p) * 128);  // wave-uniform
 #pragma unroll
             for (int t = 0; t < PT; ++t) {
                 if (l0 + t < MY) {
-                    lo[t] = buf_load16_l2(pool, olo[l0 + t] + pb);
-                    hi[t] = buf_load16_l2(pool, ohi[l0 + t] + pb);
+                    if constexpr (SOFF) {
+                        l[t] = buf_load16_l2s(pool, olo[l0 + t], pb);
+                        h[t] = buf_load16_l2s(pool, ohi[l0 + t], pb);
+                    } else {
+                        l[t] = buf_load16_l2(pool, olo[l0 + t] + pb);
+                        h[t] = buf_load16_l2(pool, ohi[l0 + t] + pb);
+                    }
                 }
             }
         };
-        load(0);
-        for (int p = 0; p < np; ++p) {
+        auto step = [&](u32x4(&l)[PT], u32x4(&h)[PT], int p) {
             u32x4 f0[PT], f1[PT];
 #pragma unroll
             for (int t = 0; t < PT; ++t)
-                if (l0 + t < MY) pair_frags(lo[t], hi[t], f0[t], f1[t], pa);
+                if (l0 + t < MY) pair_frags(l[t], h[t], f0[t], f1[t], pa, lo_first);
             const int c = 2 * rot(p);
-            if (p + 1 < np) load(p + 1);
+            if (p + DEPTH < np) load(l, h, p + DEPTH);
             if (c + 1 >= nch) {  // half piece: chunk c+1 is the zero padding chunk of the staged queries
 #pragma unroll
                 for (int t = 0; t < PT; ++t) f1[t] = u32x4{0u, 0u, 0u, 0u};
@@ -236,18 +246,29 @@ __device__ __forceinline__ void score_pairs(f32x4 (&acc)[KT][HT], const unsigned
                 for (int t = 0; t < PT; ++t)
                     if (l0 + t < MY) acc[l0 + t][u % HT] = mfma_frag<0>(u < HT ? f0[t] : f1[t], b, acc[l0 + t][u % HT]);
             }
+        };
+#pragma unroll
+        for (int s = 0; s < DEPTH; ++s)
+            if (s < np) load(lo[s], hi[s], s);
+        int p = 0;
+        for (; p + DEPTH <= np; p += DEPTH) {  // steady state: ring slot s holds piece p + s
+#pragma unroll
+            for (int s = 0; s < DEPTH; ++s) step(lo[s], hi[s], p + s);
         }
+#pragma unroll
+        for (int s = 0; s < DEPTH; ++s)
+            if (p + s < np) step(lo[s], hi[s], p + s);
     }
 }
 
-template <int HT, int KT, int PT, int MY = KT>
+template <int HT, int KT, int PT, bool SOFF, int DEPTH, int MY = KT>
 __device__ __forceinline__ void score_dispatch_pairs(int my, f32x4 (&acc)[KT][HT], const unsigned char *__restrict__ qb,
                                                      rsrc_t pool, const uint32_t (&olo)[KT],
                                                      const uint32_t (&ohi)[KT], int nch, int cr, int lane) {
     if (my == MY) {
-        score_pairs<HT, MY, KT, PT>(acc, qb, pool, olo, ohi, nch, cr, lane);
+        score_pairs<HT, MY, KT, PT, SOFF, DEPTH>(acc, qb, pool, olo, ohi, nch, cr, lane);
     } else if constexpr (MY > 1) {
-        score_dispatch_pairs<HT, KT, PT, MY - 1>(my, acc, qb, pool, olo, ohi, nch, cr, lane);
+        score_dispatch_pairs<HT, KT, PT, SOFF, DEPTH, MY - 1>(my, acc, qb, pool, olo, ohi, nch, cr, lane);
     }
 }
 
@@ -426,7 +447,7 @@ template <int HT, int KT, int NW>
 __device__ __forceinline__ void epi_target(const f32x4 (&acc)[KT][HT], const float (&mloc)[HT], int my, int nv, int w,
                                            int lane, int H, bool has_nc, float nc, float floor_log2, const float *red_m,
                                            const float *red_s, const int32_t *cslot, float *Tr) {
-    static_assert(KT <= 4, "at most 16 rows per lane");
+    static_assert(KT <= 4 || KT % 4 == 0, "tiles are reduced in groups of four");
     const int x = lane & 15, g = lane >> 4;
     const int gg = g < HT ? g : HT - 1;
     const bool head_ok = g < HT && gg * 16 + x < H;
@@ -453,24 +474,28 @@ __device__ __forceinline__ void epi_target(const f32x4 (&acc)[KT][HT], const flo
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
         wgt[ht] = (ht * 16 + x < H && mloc[ht] != -INFINITY) ? fast_exp2((mloc[ht] - fr[ht]) - lmax) * rden : 0.f;
-    float v[16];
+    // groups of four tiles: one 16-value transpose-reduction each
 #pragma unroll
-    for (int l = 0; l < 4; ++l)
+    for (int lg = 0; lg < KT; lg += 4) {
+        float v[16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float sum = 0.f;
-            if (l < KT) {
+        for (int l = 0; l < 4; ++l)
 #pragma unroll
-                for (int ht = 0; ht < HT; ++ht) sum = fmaf(acc[l][ht][i], wgt[ht], sum);
+            for (int i = 0; i < 4; ++i) {
+                float sum = 0.f;
+                if (lg + l < KT) {
+#pragma unroll
+                    for (int ht = 0; ht < HT; ++ht) sum = fmaf(acc[lg + l][ht][i], wgt[ht], sum);
+                }
+                v[4 * l + i] = sum;
             }
-            v[4 * l + i] = sum;
-        }
-    tr_step<0x128, 16>(v, (x & 8) != 0);  // row_ror:8      partner x^8
-    tr_step<0x141, 8>(v, (x & 4) != 0);   // row_half_mirror partner x^7
-    tr_step<0x4e, 4>(v, (x & 2) != 0);    // quad_perm 2301 partner x^2
-    tr_step<0xb1, 2>(v, (x & 1) != 0);    // quad_perm 1032 partner x^1
-    const int l = x >> 2, pos = 16 * (w + l * NW) + 4 * g + (x & 3);
-    if (l < KT && l < my && pos < nv) Tr[cslot[pos]] = v[0];
+        tr_step<0x128, 16>(v, (x & 8) != 0);  // row_ror:8      partner x^8
+        tr_step<0x141, 8>(v, (x & 4) != 0);   // row_half_mirror partner x^7
+        tr_step<0x4e, 4>(v, (x & 2) != 0);    // quad_perm 2301 partner x^2
+        tr_step<0xb1, 2>(v, (x & 1) != 0);    // quad_perm 1032 partner x^1
+        const int l = lg + (x >> 2), pos = 16 * (w + l * NW) + 4 * g + (x & 3);
+        if (l < KT && l < my && pos < nv) Tr[cslot[pos]] = v[0];
+    }
 }
 
 // Arguments of the target kernels (one struct in the kernel-argument segment).
@@ -586,8 +611,15 @@ __device__ __forceinline__ float window_combine(const TargetArgs &a, int lane, c
 // One workgroup per token (latest tokens first, they hold the most valid slots).  FUSED:
 // the window part of the joint softmax is computed here too (window_local) instead of being
 // read from nc_lse, so the queries are read from HBM once for the whole target.
+// Waves per SIMD the register budget is set for: 4 (128 registers) for up to 16 accumulator
+// tiles per wave, 2 (256 registers) for the 32-tile set of eight slot tiles x four head tiles.
+template <int DT, int HT, int KT>
+constexpr int waves_per_eu() {
+    return DT == 0 && KT * HT <= 16 ? 4 : 2;
+}
+
 template <int DT, int HT, int KT, int NW, bool FUSED>
-__global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kernel(const TargetArgs a) {
+__global__ __launch_bounds__(NW * 64, (waves_per_eu<DT, HT, KT>())) void distill_target_kernel(const TargetArgs a) {
     constexpr int EB = Elem<DT>::bytes;
     constexpr int KP = 2;                      // slot passes of NW*64 (K <= 2*NW*64)
     constexpr int KWT = 2;                     // window tiles per wave (W <= 128, NW >= 4)
@@ -662,12 +694,20 @@ __global__ __launch_bounds__(NW * 64, DT == 0 ? 4 : 2) void distill_target_kerne
             const int r0 = (l < my && pos < nv) ? crow[pos] : crow[0];
             const int r1 = (l < my && pos + 8 < nv) ? crow[pos + 8] : crow[0];
             olo[l] = (uint32_t)(r0 * D * EB) + pair_seg_bytes(lane);
-            ohi[l] = (uint32_t)(r1 * D * EB) + pair_seg_bytes(lane);
+            ohi[l] = (uint32_t)(r1 * D * EB) + pair_seg_bytes_hi(lane);
         }
-        constexpr int PT = KT * HT >= 16 ? 2 : KT;  // tiles per pass: 2 at the widest tile set
+        // tiles per pass: 2 with 128 registers (16 accumulator tiles), 4 with 256 (32 tiles);
+        // one piece in flight (a second one does not fit either register budget)
+        constexpr int PT = KT * HT >= 32 ? 4 : (KT * HT >= 16 ? 2 : KT);
+        constexpr int DEPTH = 1;
         const int np = (nch + 1) >> 1;
         const int cr = (5 * w + (int)(bt % np)) % np;
-        if (my > 0) score_dispatch_pairs<HT, KT, PT>(my, acc, qb, pr, olo, ohi, nch, cr, lane);
+        if (my > 0) {
+            if (nch & 1)
+                score_dispatch_pairs<HT, KT, PT, false, DEPTH>(my, acc, qb, pr, olo, ohi, nch, cr, lane);
+            else
+                score_dispatch_pairs<HT, KT, PT, true, DEPTH>(my, acc, qb, pr, olo, ohi, nch, cr, lane);
+        }
     } else {
         // fp32: lane l on row l%16 (fragment layout)
         uint32_t off[KT];

@@ -80,6 +80,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 buf_load16_l2(rsrc_t r, uint32_t byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16 /* sc1 */);
 }
+// The same with a wave-uniform part of the offset in the instruction's scalar offset, so no
+// vector add is spent on it.
+__device__ __forceinline__ u32x4 buf_load16_l2s(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 16 /* sc1 */);
+}
 
 // One fragment (8 elements) of a row at byte offset `byte_off`.
 template <int DT>
@@ -128,20 +133,20 @@ __device__ __forceinline__ u32x4 quad_to_frag(u32x4 v, int addr) {
 // chunks, 2p and 2p+1) and streams at ~48 B/clk/CU, against ~27 for 16 rows x 64 bytes.
 // A 16-row tile takes two such loads:
 //     lo: lane L holds row L/8,     16-byte segment s(L) of the piece
-//     hi: lane L holds row 8 + L/8, segment s(L)
-// with s(L) = (L%8) ^ 2*(L >= 32): the upper half-wave takes its segments in the order
-// 2,3,0,1,6,7,4,5, which keeps the permute below free of LDS bank conflicts (the lanes of
-// a row still cover one 128-byte line, so the load coalesces the same).
+//     hi: lane L holds row 8 + L/8, segment s(L) ^ 4
+// with s(L) = (L%8) ^ 2*(L >= 32): the 8 lanes of a row still cover its whole 128-byte line, so
+// both loads coalesce the same.  Because hi's segments are lo's with the chunk bit flipped, a
+// lane holds chunk 2p data in exactly one of the two registers: lanes with L%8 < 4 in lo, the
+// others in hi.  One select per dword therefore gathers each chunk into one register,
+//     A = L%8 < 4 ? lo : hi   (chunk 2p, all 16 rows)      B = L%8 < 4 ? hi : lo   (chunk 2p+1)
+// and one ds_bpermute per dword moves (row r, segment g) to fragment lane 16g + r.  Source
+// lanes (r8 = r%8, hb = r/8, x = 2*(r8 >= 4)), distinct modulo 32 within each half-wave, so
+// the permute is free of LDS bank conflicts:
+//     f0: 8*r8 + 4*hb + (g ^ x)        f1: 8*r8 + 4*(1-hb) + (g ^ x)
 __device__ __forceinline__ int pair_row_lane(int lane) { return lane >> 3; }
 __device__ __forceinline__ uint32_t pair_seg_bytes(int lane) { return (uint32_t)(16 * ((lane & 7) ^ ((lane >> 4) & 2))); }
+__device__ __forceinline__ uint32_t pair_seg_bytes_hi(int lane) { return pair_seg_bytes(lane) ^ 64u; }
 
-// Fragments of chunk 2p (f0) and chunk 2p+1 (f1) from the two loads of a tile.  A
-// bank-masked row shift first gathers each chunk into one register,
-//     A = lo on lanes L%8 < 4, hi from lane L-4 on the others   (chunk 2p, all 16 rows)
-//     B = hi from lane L+4 on lanes L%8 < 4, lo on the others   (chunk 2p+1)
-// then one ds_bpermute per dword moves (row r, segment g) to fragment lane 16g + r.
-// Source lanes (r8 = r%8, hb = r/8, x = 2*(r8 >= 4)):
-//     f0: 8*r8 + 4*hb + (g ^ x)        f1: 8*r8 + 4*(1-hb) + (g ^ x)
 struct PairAddr {
     int a0, a1;  // byte addresses for ds_bpermute
 };
@@ -149,12 +154,12 @@ __device__ __forceinline__ PairAddr pair_frag_addr(int lane) {
     const int r = lane & 15, g = lane >> 4, r8 = r & 7, hb = r >> 3, gx = g ^ (2 * (r8 >> 2));
     return PairAddr{(8 * r8 + 4 * hb + gx) << 2, (8 * r8 + 4 * (1 - hb) + gx) << 2};
 }
-__device__ __forceinline__ void pair_frags(const u32x4 &lo, const u32x4 &hi, u32x4 &f0, u32x4 &f1, PairAddr pa) {
+__device__ __forceinline__ void pair_frags(const u32x4 &lo, const u32x4 &hi, u32x4 &f0, u32x4 &f1, PairAddr pa,
+                                           bool lo_first) {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        // row_shr:4 (source lane L-4) into banks 1,3; row_shl:4 (source L+4) into banks 0,2
-        const int A = __builtin_amdgcn_update_dpp((int)lo[d], (int)hi[d], 0x114, 0xf, 0xa, false);
-        const int B = __builtin_amdgcn_update_dpp((int)lo[d], (int)hi[d], 0x104, 0xf, 0x5, false);
+        const int A = (int)(lo_first ? lo[d] : hi[d]);
+        const int B = (int)(lo_first ? hi[d] : lo[d]);
         f0[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(pa.a0, A);
         f1[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(pa.a1, B);
     }

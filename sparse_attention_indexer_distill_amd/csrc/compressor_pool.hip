@@ -15,22 +15,25 @@
 // The work is a stream over kv and score (HBM-bound; every token row is read by one or two
 // entries, the second time from L2).  Forward: one thread per (entry, CPT consecutive
 // channels), an online softmax in exp2 form over the window.  Backward: one thread per
-// (chunk of kChunk entries, CPT channels), 64 channel groups to a wave and four consecutive
-// chunks to a workgroup; for every window it recomputes the weights and the pooled value in
-// one online pass, then writes each block's dkv and dscore once (with overlap a block takes
+// (chunk of kChunk entries, CPT channels), 64 channel groups to a wave and kBwdWaves
+// consecutive chunks to a workgroup; for every window it recomputes the weights and the
+// pooled value, then writes each block's dkv and dscore once (with overlap a block takes
 // contributions from two windows, so a chunk also recomputes the first window of the next
-// chunk) and accumulates dape for its own windows in registers.  The workgroup's four waves
-// add their dape in LDS in a fixed order, and a second kernel adds the per-workgroup
-// partials in a fixed order, so every result is bitwise repeatable.
+// chunk) and accumulates dape for its own windows in registers.  Small windows (KEEP) request
+// all of the chunk's tokens, dpool rows and ape rows up front and keep them in registers, so
+// each weight costs one exp2 and no token is loaded twice by a thread; large windows make an
+// online pass and a second pass that reloads.  The workgroup's waves add their dape in LDS in
+// a fixed order, and a second kernel adds the per-workgroup partials in a fixed order, so
+// every result is bitwise repeatable.
 #include "sd_device.hpp"
 #include "sd_internal.hpp"
 
 namespace sd {
 namespace {
 
-constexpr int kChunk = 2;        // entries per backward thread
+constexpr int kChunk = 1;        // entries per backward thread
 constexpr int kPoolThreads = 256;
-constexpr int kBwdWaves = 4;     // chunks per backward workgroup, one wave each
+constexpr int kBwdWaves = 8;     // chunks per backward workgroup, one wave each
 
 // CPT consecutive channels of one row (bf16 or fp32) as fp32.
 template <int DT, int CPT>
@@ -70,10 +73,15 @@ __device__ __forceinline__ void load_f32(const float *p, float (&o)[CPT]) {
     }
 }
 
+// Output rows are written once and not read again by the kernel: streaming (non-temporal)
+// stores, which measured faster than ordinary ones for the gradient rows.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 template <int CPT>
 __device__ __forceinline__ void store_f32(float *p, const float (&v)[CPT]) {
     if constexpr (CPT == 4) {
-        *reinterpret_cast<f32x4 *>(p) = f32x4{v[0], v[1], v[2], v[3]};
+        __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(p));
+    } else if constexpr (CPT == 2) {
+        __builtin_nontemporal_store(f32x2{v[0], v[1]}, reinterpret_cast<f32x2 *>(p));
     } else {
 #pragma unroll
         for (int c = 0; c < CPT; ++c) p[c] = v[c];
@@ -187,6 +195,8 @@ __device__ __forceinline__ void window_stats(const PoolArgs &a, const int32_t *s
 template <int DT, int R, int OVL, int CPT>
 __global__ __launch_bounds__(kBwdWaves * 64) void compressor_pool_bwd_kernel(const PoolArgs a) {
     constexpr int Wc = R * (1 + OVL);
+    constexpr bool KEEP = Wc * CPT <= 16;                   // the chunk's tokens held in registers
+    constexpr int NB = kChunk + 1 + OVL;                    // KEEP: token blocks a chunk reads
     constexpr int SL = Wc * CPT <= 32 ? Wc : (32 / CPT);   // positions per LDS reduction slice
     __shared__ float red[kBwdWaves][SL][64 * CPT];
     const int G = a.D / CPT;
@@ -210,59 +220,144 @@ __global__ __launch_bounds__(kBwdWaves * 64) void compressor_pool_bwd_kernel(con
         for (int c = 0; c < CPT; ++c) dape_acc[i][c] = 0.f;
     float carry_g[OVL ? R : 1][CPT], carry_h[OVL ? R : 1][CPT];  // block n's share from window n (overlap)
 
-    for (int n = n0; n <= n_last; ++n) {
-        const int32_t seg_last = sg ? sg[R * n + R - 1] : 0;
-        float m[CPT], den[CPT], pool[CPT], dp[CPT];
-        window_stats<DT, R, OVL, CPT>(a, sg, b, n, d0, seg_last, m, den, pool);
-        load_f32<CPT>(a.dpool + (b * a.N + n) * a.D + d0, dp);
-        const bool own = n < n_own_end;
-#pragma unroll(Wc <= 16 ? Wc : 8)
-        for (int i = 0; i < Wc; ++i) {
-            const int j = R * n - OVL * R + i;
-            float gv[CPT], hv[CPT];
-            if (present<R, OVL>(sg, n, i, seg_last)) {
-                const int64_t row = b * a.S + j;
-                float s[CPT], k[CPT], ap[CPT];
-                load_ch<DT, CPT>(a.score, row * a.D + d0, s);
-                load_ch<DT, CPT>(a.kv, row * a.D + d0, k);
-                load_f32<CPT>(a.ape + (int64_t)i * a.D + d0, ap);
+    // Contributions of window n at position i (token j): dape for own windows, and the token's
+    // dkv/dscore, written once complete (with overlap a block's first share is carried).
+    auto emit = [&](int n, int i, int j, bool own, const float (&gv)[CPT], const float (&hv)[CPT]) {
+        if (own) {
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) dape_acc[i][c] += hv[c];
+        }
+        if constexpr (OVL == 0) {
+            const int64_t o = (b * a.S + j) * a.D + d0;
+            store_f32<CPT>(a.dkv + o, gv);
+            store_f32<CPT>(a.dscore + o, hv);
+        } else if (i < R) {
+            // the previous block: complete it when this thread owns it (window n-1 was its first share)
+            if (n - 1 >= n0 && j >= 0) {
+                float g2[CPT], h2[CPT];
 #pragma unroll
                 for (int c = 0; c < CPT; ++c) {
-                    const float w = fast_exp2((s[c] + ap[c]) * kLog2e - m[c]) / den[c];
-                    gv[c] = w * dp[c];
-                    hv[c] = gv[c] * (k[c] - pool[c]);
+                    g2[c] = carry_g[i][c] + gv[c];
+                    h2[c] = carry_h[i][c] + hv[c];
                 }
+                const int64_t o = (b * a.S + j) * a.D + d0;
+                store_f32<CPT>(a.dkv + o, g2);
+                store_f32<CPT>(a.dscore + o, h2);
+            }
+        } else if (own) {
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                carry_g[i - R][c] = gv[c];
+                carry_h[i - R][c] = hv[c];
+            }
+        }
+    };
+
+    if constexpr (KEEP) {
+        // Every token, dpool row and ape row the chunk needs is requested before any is used:
+        // blocks n0 - OVL .. n0 + kChunk (token t of block n0 - OVL + u at index R*u + t).
+        float ts[KEEP ? NB * R : 1][CPT], tk[KEEP ? NB * R : 1][CPT], tap[KEEP ? Wc : 1][CPT], dps[kChunk + 1][CPT];
+#pragma unroll
+        for (int u = 0; u < NB * R; ++u) {
+            const int j = R * (n0 - OVL) + u;
+            if (active && j >= 0 && j < R * (n_last + 1)) {
+                const int64_t row = b * a.S + j;
+                load_ch<DT, CPT>(a.score, row * a.D + d0, ts[u]);
+                load_ch<DT, CPT>(a.kv, row * a.D + d0, tk[u]);
             } else {
 #pragma unroll
-                for (int c = 0; c < CPT; ++c) gv[c] = hv[c] = 0.f;
+                for (int c = 0; c < CPT; ++c) ts[u][c] = tk[u][c] = 0.f;
             }
-            if (own) {
+        }
 #pragma unroll
-                for (int c = 0; c < CPT; ++c) dape_acc[i][c] += hv[c];
+        for (int q = 0; q <= kChunk; ++q) {
+            if (n0 + q <= n_last) {
+                load_f32<CPT>(a.dpool + (b * a.N + n0 + q) * a.D + d0, dps[q]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) dps[q][c] = 0.f;
             }
-            if constexpr (OVL == 0) {
-                const int64_t o = (b * a.S + j) * a.D + d0;
-                store_f32<CPT>(a.dkv + o, gv);
-                store_f32<CPT>(a.dscore + o, hv);
-            } else if (i < R) {
-                // the previous block: complete it when this thread owns it (window n-1 was its first share)
-                if (n - 1 >= n0 && j >= 0) {
-                    float g2[CPT], h2[CPT];
+        }
 #pragma unroll
-                    for (int c = 0; c < CPT; ++c) {
-                        g2[c] = carry_g[i][c] + gv[c];
-                        h2[c] = carry_h[i][c] + hv[c];
-                    }
-                    const int64_t o = (b * a.S + j) * a.D + d0;
-                    store_f32<CPT>(a.dkv + o, g2);
-                    store_f32<CPT>(a.dscore + o, h2);
-                }
-            } else if (own) {
+        for (int i = 0; i < Wc; ++i) load_f32<CPT>(a.ape + (int64_t)i * a.D + d0, tap[i]);
+
+#pragma unroll
+        for (int q = 0; q <= kChunk; ++q) {
+            const int n = n0 + q;
+            if (n > n_last) break;
+            const int32_t seg_last = sg ? sg[R * n + R - 1] : 0;
+            bool pr[Wc];    // uniform over the wave
+            float e[Wc][CPT], m[CPT], den[CPT], pool[CPT];
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) m[c] = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < Wc; ++i) {
+                pr[i] = present<R, OVL>(sg, n, i, seg_last);
 #pragma unroll
                 for (int c = 0; c < CPT; ++c) {
-                    carry_g[i - R][c] = gv[c];
-                    carry_h[i - R][c] = hv[c];
+                    e[i][c] = (ts[R * q + i][c] + tap[i][c]) * kLog2e;
+                    if (pr[i]) m[c] = fmaxf(m[c], e[i][c]);
                 }
+            }
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) den[c] = pool[c] = 0.f;
+#pragma unroll
+            for (int i = 0; i < Wc; ++i) {
+                if (!pr[i]) continue;  // absent positions take no part, whatever their values
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) {  // the entry's last token is present, so m is finite
+                    e[i][c] = fast_exp2(e[i][c] - m[c]);
+                    den[c] += e[i][c];
+                    pool[c] = fmaf(e[i][c], tk[R * q + i][c], pool[c]);
+                }
+            }
+            float gsc[CPT];  // dpool / den: the weight of position i is e_i / den
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                const float rden = 1.f / den[c];
+                pool[c] *= rden;
+                gsc[c] = dps[q][c] * rden;
+            }
+            const bool own = n < n_own_end;
+#pragma unroll
+            for (int i = 0; i < Wc; ++i) {
+                float gv[CPT], hv[CPT];
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) {
+                    gv[c] = pr[i] ? e[i][c] * gsc[c] : 0.f;
+                    hv[c] = pr[i] ? gv[c] * (tk[R * q + i][c] - pool[c]) : 0.f;
+                }
+                emit(n, i, R * n - OVL * R + i, own, gv, hv);
+            }
+        }
+    } else {
+        for (int n = n0; n <= n_last; ++n) {
+            const int32_t seg_last = sg ? sg[R * n + R - 1] : 0;
+            float m[CPT], den[CPT], pool[CPT], dp[CPT];
+            window_stats<DT, R, OVL, CPT>(a, sg, b, n, d0, seg_last, m, den, pool);
+            load_f32<CPT>(a.dpool + (b * a.N + n) * a.D + d0, dp);
+            const bool own = n < n_own_end;
+#pragma unroll(Wc <= 16 ? Wc : 8)
+            for (int i = 0; i < Wc; ++i) {
+                const int j = R * n - OVL * R + i;
+                float gv[CPT], hv[CPT];
+                if (present<R, OVL>(sg, n, i, seg_last)) {
+                    const int64_t row = b * a.S + j;
+                    float s[CPT], k[CPT], ap[CPT];
+                    load_ch<DT, CPT>(a.score, row * a.D + d0, s);
+                    load_ch<DT, CPT>(a.kv, row * a.D + d0, k);
+                    load_f32<CPT>(a.ape + (int64_t)i * a.D + d0, ap);
+#pragma unroll
+                    for (int c = 0; c < CPT; ++c) {
+                        const float wt = fast_exp2((s[c] + ap[c]) * kLog2e - m[c]) / den[c];
+                        gv[c] = wt * dp[c];
+                        hv[c] = gv[c] * (k[c] - pool[c]);
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < CPT; ++c) gv[c] = hv[c] = 0.f;
+                }
+                emit(n, i, j, own, gv, hv);
             }
         }
     }
@@ -285,7 +380,7 @@ __global__ __launch_bounds__(kBwdWaves * 64) void compressor_pool_bwd_kernel(con
             store_f32<CPT>(a.dscore + o, z);
         }
     }
-    // the workgroup's dape: its four waves (chunks) added in order, one slice of positions at a time
+    // the workgroup's dape: its waves (chunks) added in order, one slice of positions at a time
     float *part = a.dape_part + (int64_t)blockIdx.y * Wc * a.D;
 #pragma unroll
     for (int i0 = 0; i0 < Wc; i0 += SL) {
@@ -308,19 +403,35 @@ __global__ __launch_bounds__(kBwdWaves * 64) void compressor_pool_bwd_kernel(con
     }
 }
 
-// dape[x] = sum over the per-workgroup partials: wave u adds partials u, u+4, ... in order,
-// then the four wave sums are added in order (64 entries x per workgroup).
-__global__ __launch_bounds__(256) void compressor_dape_kernel(const float *__restrict__ part, int nparts,
-                                                              int64_t WcD, float *__restrict__ dape) {
-    __shared__ float red[4][64];
+// dape[x] = sum over the per-workgroup partials: wave u adds partials u, u+16, ... in order
+// (eight loads in flight), then the sixteen wave sums are added in order (64 entries x per
+// workgroup).
+constexpr int kDapeWaves = 16;
+__global__ __launch_bounds__(kDapeWaves * 64) void compressor_dape_kernel(const float *__restrict__ part, int nparts,
+                                                                          int64_t WcD, float *__restrict__ dape) {
+    __shared__ float red[kDapeWaves][64];
     const int lane = threadIdx.x & 63, u = threadIdx.x >> 6;
     const int64_t x = (int64_t)blockIdx.x * 64 + lane;
     float s = 0.f;
-    if (x < WcD)
-        for (int p = u; p < nparts; p += 4) s += part[(int64_t)p * WcD + x];
+    if (x < WcD) {
+        int p = u;
+        for (; p + 7 * kDapeWaves < nparts; p += 8 * kDapeWaves) {
+            float v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = part[(int64_t)(p + q * kDapeWaves) * WcD + x];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) s += v[q];
+        }
+        for (; p < nparts; p += kDapeWaves) s += part[(int64_t)p * WcD + x];
+    }
     red[u][lane] = s;
     __syncthreads();
-    if (u == 0 && x < WcD) dape[x] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    if (u == 0 && x < WcD) {
+        float t = red[0][lane];
+#pragma unroll
+        for (int i = 1; i < kDapeWaves; ++i) t += red[i][lane];
+        dape[x] = t;
+    }
 }
 
 template <int R, int OVL>
@@ -347,8 +458,8 @@ hipError_t launch_bwd(const PoolArgs &a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t WcD = (int64_t)Wc * a.D;
-    hipLaunchKernelGGL(compressor_dape_kernel, dim3((unsigned)((WcD + 63) / 64)), dim3(256), 0, stream, a.dape_part,
-                       a.B * a.ncb, WcD, a.dape);
+    hipLaunchKernelGGL(compressor_dape_kernel, dim3((unsigned)((WcD + 63) / 64)), dim3(kDapeWaves * 64), 0, stream,
+                       a.dape_part, a.B * a.ncb, WcD, a.dape);
     return hipGetLastError();
 }
 

@@ -28,15 +28,16 @@ constexpr int kKlRowsPerBlock = 8;
 // Loads of one row: V = 4 consecutive slots per lane and chunk (16-byte loads, K % 4 == 0)
 // or V = 1 (any K).  Lane l holds slots V*l + 64*V*c + j.  T, z and idx are loaded
 // unconditionally in one round trip (all three are K-long rows); validity is applied
-// afterwards.
+// afterwards.  The gradient row is written with streaming (non-temporal) stores: nothing
+// reads it back here, and they measured faster.
 template <int V>
 struct RowIO;
 template <>
 struct RowIO<1> {
     static __device__ __forceinline__ void load(const float *p, int k, int K, float *o) { o[0] = k < K ? p[k] : 0.f; }
     static __device__ __forceinline__ void load(const int32_t *p, int k, int K, int *o) { o[0] = k < K ? p[k] : -1; }
-    static __device__ __forceinline__ void store(float *p, int k, int K, const float *v) {
-        if (k < K) p[k] = v[0];
+    static __device__ __forceinline__ void store(float *p, int k, int K, const float *v) {  // streaming store
+        if (k < K) __builtin_nontemporal_store(v[0], p + k);
     }
 };
 template <>
@@ -57,8 +58,8 @@ struct RowIO<4> {
             o[0] = o[1] = o[2] = o[3] = -1;
         }
     }
-    static __device__ __forceinline__ void store(float *p, int k, int K, const float *v) {
-        if (k < K) *reinterpret_cast<f32x4 *>(p + k) = f32x4{v[0], v[1], v[2], v[3]};
+    static __device__ __forceinline__ void store(float *p, int k, int K, const float *v) {  // streaming store
+        if (k < K) __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(p + k));
     }
 };
 

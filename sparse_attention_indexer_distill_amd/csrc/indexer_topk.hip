@@ -12,10 +12,12 @@
 // Mapping: one wave per (b,t) row, element n of the row on lane n % 64, register n / 64,
 // so every load and every ordered prefix runs over 64 consecutive blocks.  Scores map to
 // order-preserving 32-bit keys (NaN -> 0, the smallest); the K-th largest visible key is
-// found most-significant bit first, one wave-wide count per bit (a compare and an add per
-// element on the vector unit, then one cross-lane sum), so no sort and no LDS are needed.
+// found one byte at a time, most significant first: each pass counts the visible keys that
+// share the bytes found so far into a 256-bin histogram in the wave's LDS (one atomic add per
+// key), and a suffix scan over the bins picks the next byte.  Four passes, no sort.
 // The backward is the adjoint of the gather values[k] = scores[idx[k]]: a dense row of N
-// gradients, built in LDS and streamed out with 16-byte stores.
+// gradients, built in LDS and streamed out with 16-byte stores.  Outputs are written with
+// streaming (non-temporal) stores: nothing reads them back here, and they measured faster.
 #include <math.h>
 
 #include "sd_device.hpp"
@@ -56,9 +58,11 @@ template <int E>
 __global__ __launch_bounds__(kTopkWaves * 64) void indexer_topk_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ seg, int64_t rows, int S, int N, int K, int ratio,
     int32_t *__restrict__ idx_out, float *__restrict__ val_out) {
+    __shared__ __align__(16) uint32_t hist_all[kTopkWaves][256];
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kTopkWaves + (threadIdx.x >> 6);
-    if (row >= rows) return;
+    if (row >= rows) return;  // waves never meet at a workgroup barrier: each owns its histogram
+    uint32_t *hist = hist_all[threadIdx.x >> 6];
     const int64_t b = row / S;
     const int t = (int)(row - b * S);
     const int ncomplete = (t + 1) / ratio;           // blocks complete at t
@@ -85,23 +89,47 @@ __global__ __launch_bounds__(kTopkWaves * 64) void indexer_topk_kernel(
 #pragma unroll
     for (int e = 0; e < E; ++e) count += wave_popc(vis[e]);
 
-    // Threshold: the K-th largest visible key (a visible key counts when it is >= cand, and
-    // cand >= 1 never admits an invisible one, whose key is 0).
+    // Threshold tau: the K-th largest visible key, built a byte at a time.  Invariant: the
+    // visible keys above the bytes found so far number fewer than K, and `need` of the keys
+    // that share them are still to be taken.
     uint32_t tau = 0u;
     int need = count;  // how many of the keys equal to tau are kept (in ascending block order)
     if (count > K) {
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cand = tau | (1u << bit);
-            // per-lane counts on the vector unit, then one wave sum (exact in fp32: <= 4096)
-            int c = 0;
+        need = K;
+        uint32_t hmask = 0u;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            *reinterpret_cast<u32x4 *>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+            wave_lds_order();
 #pragma unroll
-            for (int e = 0; e < E; ++e) c += key[e] >= cand ? 1 : 0;
-            if (wave_sum((float)c) >= (float)K) tau = cand;
+            for (int e = 0; e < E; ++e)
+                if (vis[e] && (key[e] & hmask) == tau) atomicAdd(hist + ((key[e] >> shift) & 255u), 1u);
+            wave_lds_order();
+            const u32x4 h = *reinterpret_cast<const u32x4 *>(hist + 4 * lane);   // bins 4*lane .. 4*lane+3
+            const int own = (int)(h[0] + h[1] + h[2] + h[3]);
+            int suf = own;  // keys in the bins of this lane and of every higher lane
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int t = __shfl_down(suf, d);
+                suf += lane + d < 64 ? t : 0;
+            }
+            // the byte's lane: the highest one whose suffix still reaches `need`
+            const int L = __popcll(__ballot(suf >= need)) - 1;
+            const int above = __shfl(suf - own, L);   // keys in bins above lane L's four
+            const u32x4 hl = {(uint32_t)__shfl((int)h[0], L), (uint32_t)__shfl((int)h[1], L),
+                              (uint32_t)__shfl((int)h[2], L), (uint32_t)__shfl((int)h[3], L)};
+            int cum = above, dig = 4 * L;
+#pragma unroll
+            for (int j = 3; j >= 0; --j) {
+                if (cum + (int)hl[j] >= need) {
+                    dig = 4 * L + j;
+                    break;
+                }
+                cum += (int)hl[j];
+            }
+            need -= cum;  // keys above the chosen bin are all taken
+            tau |= (uint32_t)dig << shift;
+            hmask |= 255u << shift;
         }
-        int greater = 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) greater += wave_popc(vis[e] && key[e] > tau);
-        need = K - greater;
     }
 
     int32_t *io = idx_out + row * K;
@@ -119,14 +147,14 @@ __global__ __launch_bounds__(kTopkWaves * 64) void indexer_topk_kernel(
         const uint64_t sm = __ballot(sel);
         if (sel) {
             const int pos = pos_base + wave_prefix(sm);
-            io[pos] = 64 * e + lane;
-            if (vo) vo[pos] = val[e];
+            __builtin_nontemporal_store(64 * e + lane, io + pos);
+            if (vo) __builtin_nontemporal_store(val[e], vo + pos);
         }
         pos_base += __popcll(sm);
     }
     for (int k = pos_base + lane; k < K; k += 64) {  // slots left over
-        io[k] = -1;
-        if (vo) vo[k] = -INFINITY;
+        __builtin_nontemporal_store(-1, io + k);
+        if (vo) __builtin_nontemporal_store(-INFINITY, vo + k);
     }
 }
 
@@ -182,7 +210,7 @@ __global__ __launch_bounds__(kTopkWaves * 64) void indexer_topk_bwd_kernel(
     float *o = dscores + row * N;
     if ((N & 3) == 0) {
         for (int n = 4 * lane; n < N; n += 256)
-            *reinterpret_cast<f32x4 *>(o + n) = *reinterpret_cast<const f32x4 *>(buf + n);
+            __builtin_nontemporal_store(*reinterpret_cast<const f32x4 *>(buf + n), reinterpret_cast<f32x4 *>(o + n));
     } else {
         for (int n = lane; n < N; n += 64) o[n] = buf[n];
     }

@@ -69,8 +69,8 @@ enum { SD_BF16 = 0, SD_F32 = 1 };
  *   seg    [B,S]      int32 or NULL   packed-segment ids; NULL = one segment
  *   nc_lse [B,S,H]    float32 out     natural-log mass (never -inf: j = t is in win(t))
  * Limits: D % 32 == 0, D <= 512; H <= 64; 1 <= W <= 128; S * D * element size < 2^31
- * bytes (one batch row of kwin); S <= 2^24 - 2 (the grid has one 512-lane workgroup per
- * two tokens, and a dispatch counts at most 2^32 - 1 work-items).
+ * bytes (one batch row of kwin) and S <= 2^24 rows; S <= 2^24 - 2 (the grid has one
+ * 512-lane workgroup per two tokens, and a dispatch counts at most 2^32 - 1 work-items).
  */
 int window_lse(const void *q, const void *kwin, const float *sink, const int32_t *seg,
                int B, int S, int H, int D, int W, float scale, int dtype, float *nc_lse,
@@ -101,7 +101,7 @@ int window_lse(const void *q, const void *kwin, const float *sink, const int32_t
  *   l1_floor         <= 0 selects FLT_MIN (2^-126); 1e-10 reproduces the legacy floor
  *   target [B,S,K]   float32 out      a row with no valid slot is all zeros
  * Limits: D % 32 == 0, D <= 512; H <= 64; K <= 1024; N * D * element size < 2^31 bytes
- * (one batch row of pool); B * S < 2^22 (one workgroup of up to 1024 lanes per token, and a
+ * (one batch row of pool) and N <= 2^24 rows; B * S < 2^22 (one workgroup of up to 1024 lanes per token, and a
  * dispatch counts at most 2^32 - 1 work-items).  A non-positive or non-finite scale is rejected with
  * SD_ERR_BAD_SHAPE.
  */

@@ -41,6 +41,32 @@ def _compile(src: str) -> str:
     return obj
 
 
+def kernel_resources(src: str) -> dict:
+    """Registers, scratch (spill) bytes and occupancy the compiler reports for every kernel of
+    one source file, from a device-only compile with the library's flags:
+    {mangled name: {"vgpr": n, "agpr": n, "scratch": bytes per lane, "occupancy": waves per SIMD}}."""
+    path = src if os.path.isabs(src) else os.path.join(CSRC, src)
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(path), []), "--cuda-device-only",
+           "-Rpass-analysis=kernel-resource-usage", "-c", path, "-o", os.devnull]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {path}:\n{r.stderr[-4000:]}")
+    out, cur = {}, None
+    keys = {"VGPRs": "vgpr", "AGPRs": "agpr", "ScratchSize [bytes/lane]": "scratch", "Occupancy [waves/SIMD]": "occupancy"}
+    for line in r.stderr.splitlines():
+        if "remark:" not in line:
+            continue
+        body = line.split("remark:", 1)[1].split("[-Rpass-analysis")[0].strip()
+        if body.startswith("Function Name:"):
+            cur = body.split(":", 1)[1].strip()
+            out[cur] = {}
+        elif cur is not None and ":" in body:
+            k, v = body.rsplit(":", 1)
+            if k.strip() in keys:
+                out[cur][keys[k.strip()]] = int(v.strip())
+    return out
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ_DIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))

@@ -44,12 +44,15 @@ int check_common(int dtype, int B, int S, int H, int D) {
 
 // The kernels address one batch row of pool or window keys through a 32-bit buffer range
 // with 32-bit signed row offsets (row * D * element size), so each such row must stay
-// below 2^31 bytes.
+// below 2^31 bytes; row indices are multiplied in 24 bits, so at most 2^24 rows.
 int check_rows(const char *fn, const char *what, int64_t rows, int D, int dtype) {
     const int64_t eb = dtype == SD_F32 ? 4 : 2;
     if (rows * D * eb > (((int64_t)1 << 31) - 1))
         return fail(SD_ERR_UNSUPPORTED, "%s: %s of %lld rows x D=%d exceeds 2^31 bytes per batch", fn, what,
                     (long long)rows, D);
+    if (rows > ((int64_t)1 << 24))
+        return fail(SD_ERR_UNSUPPORTED, "%s: %s of %lld rows exceeds 2^24 rows per batch", fn, what,
+                    (long long)rows);
     return SD_OK;
 }
 

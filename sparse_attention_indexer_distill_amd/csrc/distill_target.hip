@@ -226,8 +226,8 @@ __device__ __forceinline__ void score_pairs(f32x4 (&acc)[KT][HT], const unsigned
                 if (l0 + t < MY) pair_frags(l[t], h[t], f0[t], f1[t], pa, lo_first);
             const int c = 2 * rot(p);
             if (p + DEPTH < np) load(l, h, p + DEPTH);
-            if (c + 1 >= nch) {  // half piece: chunk c+1 is the zero padding chunk of the staged queries
-#pragma unroll
+            if (!SOFF && c + 1 >= nch) {  // half piece (odd chunk counts only): chunk c+1 is the
+#pragma unroll                                // zero padding chunk of the staged queries
                 for (int t = 0; t < PT; ++t) f1[t] = u32x4{0u, 0u, 0u, 0u};
             }
             // query blocks of the pair: chunk c from the even-parity base, c+1 from the odd one,
@@ -568,18 +568,23 @@ __device__ __forceinline__ void window_local(const TargetArgs &a, const unsigned
         }
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-        float mx = -INFINITY;
+        // masked keys become -inf (whatever they hold), so the maximum and the exponentials
+        // need no further masks; the maximum is taken before scaling (scale > 0)
 #pragma unroll
         for (int l = 0; l < KWT; ++l)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mx = okj[l][i] ? fmaxf(mx, acc[l][ht][i] * a.scale_log2) : mx;
-        mx = cols4_max(mx);
+            for (int i = 0; i < 4; ++i) acc[l][ht][i] = okj[l][i] ? acc[l][ht][i] : -INFINITY;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int l = 0; l < KWT; ++l)
+            mx = fmaxf(mx, fmaxf(fmaxf(acc[l][ht][0], acc[l][ht][1]), fmaxf(acc[l][ht][2], acc[l][ht][3])));
+        mx = cols4_max(mx) * a.scale_log2;  // -inf when this wave holds no valid key
+        const float nm = mx == -INFINITY ? 0.f : -mx;
         float sum = 0.f;
 #pragma unroll
         for (int l = 0; l < KWT; ++l)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sum += okj[l][i] ? fast_exp2(fmaf(acc[l][ht][i], a.scale_log2, -mx)) : 0.f;
+            for (int i = 0; i < 4; ++i) sum += fast_exp2(fmaf(acc[l][ht][i], a.scale_log2, nm));
         sum = cols4_sum(sum);
         if (lane < 16) {
             red_wm[(w * 16 + x) * HT + ht] = mx;
@@ -693,8 +698,9 @@ __global__ __launch_bounds__(NW * 64, (waves_per_eu<DT, HT, KT>())) void distill
             const int pos = 16 * (w + l * NW) + pair_row_lane(lane);
             const int r0 = (l < my && pos < nv) ? crow[pos] : crow[0];
             const int r1 = (l < my && pos + 8 < nv) ? crow[pos + 8] : crow[0];
-            olo[l] = (uint32_t)(r0 * D * EB) + pair_seg_bytes(lane);
-            ohi[l] = (uint32_t)(r1 * D * EB) + pair_seg_bytes_hi(lane);
+            // 24-bit multiplies (rows < 2^24): 32-bit results, no 64-bit register pairs
+            olo[l] = __umul24((uint32_t)r0, (uint32_t)(D * EB)) + pair_seg_bytes(lane);
+            ohi[l] = __umul24((uint32_t)r1, (uint32_t)(D * EB)) + pair_seg_bytes_hi(lane);
         }
         // tiles per pass: 2 with 128 registers (16 accumulator tiles), 4 with 256 (32 tiles);
         // one piece in flight (a second one does not fit either register budget)

@@ -103,6 +103,10 @@ def test_distill_target_rejections(lib):
     assert _tg(lib, H=128) == sd.SD_ERR_UNSUPPORTED
     assert _tg(lib, N=1 << 21, D=512) == sd.SD_ERR_UNSUPPORTED           # pool row of 2^31 bytes
     assert b"pool" in lib.sd_last_error()
+    # row indices are multiplied in 24 bits: at most 2^24 pool rows, even where the bytes fit
+    assert _tg(lib, N=(1 << 24) + 1, D=32) == sd.SD_ERR_UNSUPPORTED
+    assert b"2^24 rows" in lib.sd_last_error()
+    assert _tf(lib, N=(1 << 24) + 1, D=32) == sd.SD_ERR_UNSUPPORTED
     # up to 1024 lanes per token: B*S must stay below 2^22
     assert _tg(lib, B=1, S=1 << 22, H=1) == sd.SD_ERR_UNSUPPORTED
     assert b"2^22" in lib.sd_last_error()

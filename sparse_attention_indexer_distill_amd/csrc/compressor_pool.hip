@@ -213,20 +213,16 @@ __global__ __launch_bounds__(kBwdWaves * 64) void compressor_pool_bwd_kernel(con
     // with overlap, block n_own_end - 1 also takes a contribution from window n_own_end
     const int n_last = !active ? n0 - 1 : (OVL && n_own_end < a.N ? n_own_end : n_own_end - 1);
 
-    float dape_acc[Wc][CPT];
+    float dape_acc[KEEP ? Wc : 1][CPT];  // KEEP: this thread's dape (large windows reduce in LDS as they go)
 #pragma unroll
-    for (int i = 0; i < Wc; ++i)
+    for (int i = 0; i < (KEEP ? Wc : 1); ++i)
 #pragma unroll
         for (int c = 0; c < CPT; ++c) dape_acc[i][c] = 0.f;
     float carry_g[OVL ? R : 1][CPT], carry_h[OVL ? R : 1][CPT];  // block n's share from window n (overlap)
 
-    // Contributions of window n at position i (token j): dape for own windows, and the token's
-    // dkv/dscore, written once complete (with overlap a block's first share is carried).
+    // dkv/dscore of window n at position i (token j), written once complete (with overlap a
+    // block's first share is carried).
     auto emit = [&](int n, int i, int j, bool own, const float (&gv)[CPT], const float (&hv)[CPT]) {
-        if (own) {
-#pragma unroll
-            for (int c = 0; c < CPT; ++c) dape_acc[i][c] += hv[c];
-        }
         if constexpr (OVL == 0) {
             const int64_t o = (b * a.S + j) * a.D + d0;
             store_f32<CPT>(a.dkv + o, gv);
@@ -327,42 +323,83 @@ __global__ __launch_bounds__(kBwdWaves * 64) void compressor_pool_bwd_kernel(con
                     gv[c] = pr[i] ? e[i][c] * gsc[c] : 0.f;
                     hv[c] = pr[i] ? gv[c] * (tk[R * q + i][c] - pool[c]) : 0.f;
                 }
+                if (own) {
+#pragma unroll
+                    for (int c = 0; c < CPT; ++c) dape_acc[KEEP ? i : 0][c] += hv[c];
+                }
                 emit(n, i, R * n - OVL * R + i, own, gv, hv);
             }
         }
     } else {
-        for (int n = n0; n <= n_last; ++n) {
-            const int32_t seg_last = sg ? sg[R * n + R - 1] : 0;
-            float m[CPT], den[CPT], pool[CPT], dp[CPT];
-            window_stats<DT, R, OVL, CPT>(a, sg, b, n, d0, seg_last, m, den, pool);
-            load_f32<CPT>(a.dpool + (b * a.N + n) * a.D + d0, dp);
-            const bool own = n < n_own_end;
-#pragma unroll(Wc <= 16 ? Wc : 8)
-            for (int i = 0; i < Wc; ++i) {
-                const int j = R * n - OVL * R + i;
+        // Large windows, one own window per thread (kChunk == 1): an online pass for the
+        // statistics, then the gradient pass reloads each position; the own window's dape goes
+        // to LDS slice by slice and is reduced over the workgroup at once (no per-position
+        // accumulators).  With overlap, window n0 + 1 then completes block n0.
+        static_assert(kChunk == 1, "large windows reduce one own window per thread");
+        auto grad = [&](bool live, int n, int i, int32_t seg_last, const float (&m)[CPT], const float (&den)[CPT],
+                        const float (&pool)[CPT], const float (&dp)[CPT], float (&gv)[CPT], float (&hv)[CPT]) {
+            const bool pres = live && present<R, OVL>(sg, n, i, seg_last);
+            float sc[CPT] = {}, k[CPT] = {}, ap[CPT] = {};
+            if (pres) {
+                const int64_t row = b * a.S + (R * n - OVL * R + i);
+                load_ch<DT, CPT>(a.score, row * a.D + d0, sc);
+                load_ch<DT, CPT>(a.kv, row * a.D + d0, k);
+                load_f32<CPT>(a.ape + (int64_t)i * a.D + d0, ap);
+            }
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                const float g = fast_exp2((sc[c] + ap[c]) * kLog2e - m[c]) / den[c] * dp[c];
+                gv[c] = pres ? g : 0.f;
+                hv[c] = pres ? g * (k[c] - pool[c]) : 0.f;
+            }
+        };
+        float m[CPT] = {}, den[CPT] = {}, pool[CPT] = {}, dp[CPT] = {};
+        int32_t seg_last = 0;
+        if (active) {
+            seg_last = sg ? sg[R * n0 + R - 1] : 0;
+            window_stats<DT, R, OVL, CPT>(a, sg, b, n0, d0, seg_last, m, den, pool);
+            load_f32<CPT>(a.dpool + (b * a.N + n0) * a.D + d0, dp);
+        }
+        float *part = a.dape_part + (int64_t)blockIdx.y * Wc * a.D;
+        for (int i0 = 0; i0 < Wc; i0 += SL) {
+#pragma unroll
+            for (int ii = 0; ii < SL; ++ii) {
                 float gv[CPT], hv[CPT];
-                if (present<R, OVL>(sg, n, i, seg_last)) {
-                    const int64_t row = b * a.S + j;
-                    float s[CPT], k[CPT], ap[CPT];
-                    load_ch<DT, CPT>(a.score, row * a.D + d0, s);
-                    load_ch<DT, CPT>(a.kv, row * a.D + d0, k);
-                    load_f32<CPT>(a.ape + (int64_t)i * a.D + d0, ap);
+                grad(active, n0, i0 + ii, seg_last, m, den, pool, dp, gv, hv);
+                if (active) emit(n0, i0 + ii, R * n0 - OVL * R + i0 + ii, true, gv, hv);
 #pragma unroll
-                    for (int c = 0; c < CPT; ++c) {
-                        const float wt = fast_exp2((s[c] + ap[c]) * kLog2e - m[c]) / den[c];
-                        gv[c] = wt * dp[c];
-                        hv[c] = gv[c] * (k[c] - pool[c]);
-                    }
-                } else {
+                for (int c = 0; c < CPT; ++c) red[w][ii][lane * CPT + c] = hv[c];
+            }
+            __syncthreads();
+            for (int e = threadIdx.x; e < SL * 64 * CPT; e += kBwdWaves * 64) {
+                const int ii = e / (64 * CPT), x = e - ii * (64 * CPT);
+                const int d = blockIdx.x * 64 * CPT + x;
+                if (d < a.D) {
+                    float v = red[0][ii][x];
 #pragma unroll
-                    for (int c = 0; c < CPT; ++c) gv[c] = hv[c] = 0.f;
+                    for (int u = 1; u < kBwdWaves; ++u) v += red[u][ii][x];
+                    part[(int64_t)(i0 + ii) * a.D + d] = v;
                 }
-                emit(n, i, j, own, gv, hv);
+            }
+            __syncthreads();
+        }
+        if (OVL && active && n_last > n0) {  // window n0 + 1: its first R positions complete block n0
+            const int n = n0 + 1;
+            const int32_t sl = sg ? sg[R * n + R - 1] : 0;
+            float m1[CPT], den1[CPT], pool1[CPT], dp1[CPT];
+            window_stats<DT, R, OVL, CPT>(a, sg, b, n, d0, sl, m1, den1, pool1);
+            load_f32<CPT>(a.dpool + (b * a.N + n) * a.D + d0, dp1);
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                float gv[CPT], hv[CPT];
+                grad(true, n, i, sl, m1, den1, pool1, dp1, gv, hv);
+                emit(n, i, R * n - OVL * R + i, false, gv, hv);
             }
         }
     }
     if constexpr (OVL == 1) {
         if (active && n_own_end == a.N) {  // the last block has no later window
+#pragma unroll
             for (int i = 0; i < R; ++i) {
                 const int64_t o = (b * a.S + (int64_t)R * (a.N - 1) + i) * a.D + d0;
                 store_f32<CPT>(a.dkv + o, carry_g[i]);
@@ -380,14 +417,16 @@ __global__ __launch_bounds__(kBwdWaves * 64) void compressor_pool_bwd_kernel(con
             store_f32<CPT>(a.dscore + o, z);
         }
     }
-    // the workgroup's dape: its waves (chunks) added in order, one slice of positions at a time
+    // KEEP: the workgroup's dape, its waves (chunks) added in order, one slice of positions at
+    // a time (large windows have done this above)
+    if constexpr (!KEEP) return;
     float *part = a.dape_part + (int64_t)blockIdx.y * Wc * a.D;
 #pragma unroll
     for (int i0 = 0; i0 < Wc; i0 += SL) {
 #pragma unroll
         for (int ii = 0; ii < SL; ++ii)
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) red[w][ii][lane * CPT + c] = dape_acc[i0 + ii][c];
+            for (int c = 0; c < CPT; ++c) red[w][ii][lane * CPT + c] = dape_acc[KEEP ? i0 + ii : 0][c];
         __syncthreads();
         for (int e = threadIdx.x; e < SL * 64 * CPT; e += kBwdWaves * 64) {
             const int ii = e / (64 * CPT), x = e - ii * (64 * CPT);

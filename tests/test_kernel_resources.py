@@ -45,3 +45,10 @@ def test_hot_kernel_has_no_spills(resources, src, pattern, occ):
     (name, r), = found.items()
     assert r["scratch"] == 0, f"{name} spills {r['scratch']} bytes per lane ({r})"
     assert r["occupancy"] >= occ, f"{name}: occupancy {r['occupancy']} waves/SIMD < {occ} ({r})"
+
+
+@pytest.mark.parametrize("src", ["compressor_pool.hip", "indexer_topk.hip", "distill_kl.hip"])
+def test_every_instantiation_has_no_spills(resources, src):
+    """The next-row kernels and the KL, at every ratio, window and width they are built for."""
+    bad = {k: v for k, v in resources[src].items() if v["scratch"] > 0}
+    assert not bad, f"{src}: {bad}"

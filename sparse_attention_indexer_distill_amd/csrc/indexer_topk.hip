@@ -91,7 +91,8 @@ __global__ __launch_bounds__(kTopkWaves * 64) void indexer_topk_kernel(
 
     // Threshold tau: the K-th largest visible key, built a byte at a time.  Invariant: the
     // visible keys above the bytes found so far number fewer than K, and `need` of the keys
-    // that share them are still to be taken.
+    // that share them are still to be taken.  When a pass takes its whole bin, the remaining
+    // bytes of tau stay 0 and every key >= tau is kept (exactly K of them).
     uint32_t tau = 0u;
     int need = count;  // how many of the keys equal to tau are kept (in ascending block order)
     if (count > K) {
@@ -117,11 +118,12 @@ __global__ __launch_bounds__(kTopkWaves * 64) void indexer_topk_kernel(
             const int above = __shfl(suf - own, L);   // keys in bins above lane L's four
             const u32x4 hl = {(uint32_t)__shfl((int)h[0], L), (uint32_t)__shfl((int)h[1], L),
                               (uint32_t)__shfl((int)h[2], L), (uint32_t)__shfl((int)h[3], L)};
-            int cum = above, dig = 4 * L;
+            int cum = above, dig = 4 * L, inbin = 0;
 #pragma unroll
             for (int j = 3; j >= 0; --j) {
                 if (cum + (int)hl[j] >= need) {
                     dig = 4 * L + j;
+                    inbin = (int)hl[j];
                     break;
                 }
                 cum += (int)hl[j];
@@ -129,6 +131,10 @@ __global__ __launch_bounds__(kTopkWaves * 64) void indexer_topk_kernel(
             need -= cum;  // keys above the chosen bin are all taken
             tau |= (uint32_t)dig << shift;
             hmask |= 255u << shift;
+            if (need == inbin) {  // the whole bin is taken: keep every key >= tau (lower bytes 0)
+                need = K;
+                break;
+            }
         }
     }
 

@@ -517,8 +517,9 @@ struct TargetArgs {
 // Window part of the joint softmax for token t of batch b, inside the target kernel:
 // the LSE over {scale <q_h, kwin_j> : j in [max(0, t-W+1), t], seg[j] == seg[t]} plus the
 // sink, per head.  Window tiles of 16 consecutive keys starting at the first key are dealt
-// in pairs: wave w scores tiles 2w and 2w+1 together in one pass of the same MFMA loop, so
-// each pair reads the staged queries once (half the query reads of one tile per wave).
+// KWT to a wave: wave w scores tiles KWT*w .. KWT*w + KWT-1 together in one pass of the same
+// MFMA loop, so a pair reads the staged queries once (half the query reads of one tile per
+// wave).
 // window_local publishes each wave's masked per-head maximum and sum in red_wm/red_ws
 // without waiting; after the epilogue's barrier window_combine reduces them over the waves
 // and adds the sink, returning in natural log the value of head 16*min(g, HT-1) + x for
@@ -530,7 +531,7 @@ __device__ __forceinline__ void window_local(const TargetArgs &a, const unsigned
     const int S = a.S, D = a.D, nch = D >> 5;
     const int kf = t - a.W + 1 > 0 ? t - a.W + 1 : 0;
     const int nwt = (t - kf + 16) >> 4;                                 // at most 8 (W <= 128)
-    const int myw = nwt - 2 * w >= 2 ? 2 : (nwt - 2 * w > 0 ? nwt - 2 * w : 0);  // tiles 2w, 2w+1
+    const int myw = nwt - KWT * w >= KWT ? KWT : (nwt - KWT * w > 0 ? nwt - KWT * w : 0);  // tiles KWT*w + l
     const rsrc_t kr = make_rsrc(reinterpret_cast<const char *>(a.kwin) + (size_t)b * S * D * EB,
                                 (uint32_t)((size_t)S * D * EB));
     f32x4 acc[KWT][HT];
@@ -544,7 +545,7 @@ __device__ __forceinline__ void window_local(const TargetArgs &a, const unsigned
         uint32_t off[KWT];
 #pragma unroll
         for (int l = 0; l < KWT; ++l) {
-            int r = kf + 16 * (2 * w + l) + (DT == 0 ? (int)quad_row_lane(lane) : (lane & 15));
+            int r = kf + 16 * (KWT * w + l) + (DT == 0 ? (int)quad_row_lane(lane) : (lane & 15));
             r = r < t ? r : t;  // rows past t are loaded as row t and masked below
             off[l] = DT == 0 ? (uint32_t)(r * D * EB) + quad_seg_bytes(lane)
                              : (uint32_t)((r * D + 8 * (lane >> 4)) * EB);
@@ -555,7 +556,7 @@ __device__ __forceinline__ void window_local(const TargetArgs &a, const unsigned
             score_dispatch_f32<HT, KWT>(myw, acc, qb, RS, kr, off, nch, lane);
         }
     }
-    // masked statistics (log2 domain); key j of element (l, i) = kf + 16(2w + l) + 4g + i
+    // masked statistics (log2 domain); key j of element (l, i) = kf + 16(KWT w + l) + 4g + i
     const int x = lane & 15, g = lane >> 4;
     const int sg_t = a.seg ? a.seg[(size_t)b * S + t] : 0;
     bool okj[KWT][4];
@@ -563,7 +564,7 @@ __device__ __forceinline__ void window_local(const TargetArgs &a, const unsigned
     for (int l = 0; l < KWT; ++l)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int j = kf + 16 * (2 * w + l) + 4 * g + i;
+            const int j = kf + 16 * (KWT * w + l) + 4 * g + i;
             okj[l][i] = l < myw && j <= t && (a.seg == nullptr || a.seg[(size_t)b * S + j] == sg_t);
         }
 #pragma unroll
@@ -627,8 +628,10 @@ template <int DT, int HT, int KT, int NW, bool FUSED>
 __global__ __launch_bounds__(NW * 64, (waves_per_eu<DT, HT, KT>())) void distill_target_kernel(const TargetArgs a) {
     constexpr int EB = Elem<DT>::bytes;
     constexpr int KP = 2;                      // slot passes of NW*64 (K <= 2*NW*64)
-    constexpr int KWT = 2;                     // window tiles per wave (W <= 128, NW >= 4)
-    static_assert(!FUSED || NW >= 4, "the eight window tiles need four waves at two tiles each");
+    // window tiles per wave (W <= 128): pairs on waves 0-3 with 8 waves (one read of the staged
+    // queries per pair), single tiles on waves 0-7 with 16 (one workgroup per CU: balance wins)
+    constexpr int KWT = NW >= 16 ? 1 : 2;
+    static_assert(!FUSED || NW * KWT >= 8, "the eight window tiles need NW * KWT >= 8");
     extern __shared__ __align__(16) unsigned char smem[];
     const int S = a.S, H = a.H, D = a.D, N = a.N, K = a.K;
     const int nch = D >> 5;

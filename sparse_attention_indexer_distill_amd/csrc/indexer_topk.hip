@@ -168,6 +168,9 @@ __global__ __launch_bounds__(kTopkWaves * 64) void indexer_topk_kernel(
 // every other block.  Slot indices are first written into the wave's LDS row as tags: if every
 // valid slot reads its own tag back, the row's slots are distinct and each block receives
 // one gradient by a plain store; otherwise the gradients are added one slot at a time.
+// KE > 0: the row's K <= 64 KE slots and gradients are loaded once into registers (slot
+// 64 e + lane in register e); KE == 0 reads them from memory in each pass (any K).
+template <int KE>
 __global__ __launch_bounds__(kTopkWaves * 64) void indexer_topk_bwd_kernel(
     const float *__restrict__ dval, const int32_t *__restrict__ idx, int64_t rows, int N, int K,
     float *__restrict__ dscores) {
@@ -179,35 +182,52 @@ __global__ __launch_bounds__(kTopkWaves * 64) void indexer_topk_bwd_kernel(
     float *buf = reinterpret_cast<float *>(tag);
     const int32_t *ir = idx + row * K;
     const float *dr = dval + row * K;
+    constexpr int R = KE > 0 ? KE : 1;
+    int sn[R];
+    float sgv[R];
+    if constexpr (KE > 0) {
+#pragma unroll
+        for (int e = 0; e < KE; ++e) {
+            const int k = 64 * e + lane;
+            sn[e] = k < K ? ir[k] : -1;
+            sgv[e] = k < K ? dr[k] : 0.f;
+        }
+    }
+    // slot k of this lane's e-th step and its block (-1 when invalid or past K)
+    auto slot = [&](int e, int k) -> int {
+        int n;
+        if constexpr (KE > 0) n = sn[e];
+        else n = k < K ? ir[k] : -1;
+        return n >= 0 && n < N ? n : -1;
+    };
+    const int steps = KE > 0 ? KE : (K + 63) / 64;
 
     for (int n = lane; n < N; n += 64) tag[n] = 0xffffffffu;
     wave_lds_order();
-    for (int k = lane; k < K; k += 64) {
-        const int n = ir[k];
-        if (n >= 0 && n < N) tag[n] = (uint32_t)k;
+    for (int e = 0; e < steps; ++e) {
+        const int k = 64 * e + lane, n = slot(e, k);
+        if (n >= 0) tag[n] = (uint32_t)k;
     }
     wave_lds_order();
     bool dup = false;
-    for (int k = lane; k < K; k += 64) {
-        const int n = ir[k];
-        if (n >= 0 && n < N) dup = dup || tag[n] != (uint32_t)k;
+    for (int e = 0; e < steps; ++e) {
+        const int k = 64 * e + lane, n = slot(e, k);
+        if (n >= 0) dup = dup || tag[n] != (uint32_t)k;
     }
     const bool any_dup = __ballot(dup) != 0;
     wave_lds_order();
     for (int n = lane; n < N; n += 64) buf[n] = 0.f;
     wave_lds_order();
-    if (!any_dup) {
-        for (int k = lane; k < K; k += 64) {
-            const int n = ir[k];
-            if (n >= 0 && n < N) buf[n] = dr[k];
-        }
-    } else {
-        for (int k0 = 0; k0 < K; k0 += 64) {
-            const int k = k0 + lane;
-            const int n = k < K ? ir[k] : -1;
-            const float g = k < K ? dr[k] : 0.f;
-            for (int j = 0; j < 64; ++j) {  // slot order within the chunk
-                if (lane == j && n >= 0 && n < N) buf[n] += g;
+    for (int e = 0; e < steps; ++e) {
+        const int k = 64 * e + lane, n = slot(e, k);
+        float g;
+        if constexpr (KE > 0) g = sgv[e];
+        else g = k < K ? dr[k] : 0.f;
+        if (!any_dup) {
+            if (n >= 0) buf[n] = g;
+        } else {
+            for (int j = 0; j < 64; ++j) {  // slot order within the step
+                if (lane == j && n >= 0) buf[n] += g;
                 wave_lds_order();
             }
         }
@@ -250,8 +270,15 @@ hipError_t launch_indexer_topk_bwd(const float *dvalues, const int32_t *idx, int
     const int64_t rows = (int64_t)B * S;
     const unsigned grid = (unsigned)((rows + kTopkWaves - 1) / kTopkWaves);
     const size_t lds = (size_t)kTopkWaves * N * sizeof(float);  // <= 64 KiB for N <= 4096
-    hipLaunchKernelGGL(indexer_topk_bwd_kernel, dim3(grid), dim3(kTopkWaves * 64), lds, stream, dvalues, idx, rows,
-                       N, K, dscores);
+#define SD_TB(KE) hipLaunchKernelGGL(indexer_topk_bwd_kernel<KE>, dim3(grid), dim3(kTopkWaves * 64), lds, stream, \
+                                     dvalues, idx, rows, N, K, dscores)
+    if (K <= 64) SD_TB(1);
+    else if (K <= 128) SD_TB(2);
+    else if (K <= 256) SD_TB(4);
+    else if (K <= 512) SD_TB(8);
+    else if (K <= 1024) SD_TB(16);
+    else SD_TB(0);
+#undef SD_TB
     return hipGetLastError();
 }
 

@@ -129,6 +129,42 @@ def test_topk_bwd_scatter_bit_exact_and_duplicates():
     np.testing.assert_array_equal(got[nodup], ref[nodup].astype(np.float32).astype(np.float64))
 
 
+@pytest.mark.parametrize("K,N", [(1, 7), (37, 130), (100, 301), (200, 257), (333, 1000), (700, 1500),
+                                 (1000, 1024), (1100, 2048), (2100, 4096), (4096, 4096)])
+def test_topk_bwd_scatter_ragged_slot_counts(K, N):
+    """Slot counts on both sides of every register width of the scatter and past it (K above 1024
+    reads the slots from memory), 97 rows (a ragged last workgroup), invalid slots, and rows whose
+    duplicate slots lie 64 or more slots apart (different register steps)."""
+    sd = _sd()
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(1000 + K)
+    S = 97
+    if K <= N:
+        idx = np.argsort(rng.random((1, S, N)), axis=-1)[..., :K].astype(np.int32)
+    else:
+        idx = rng.integers(0, N, size=(1, S, K)).astype(np.int32)
+    junk = rng.random(idx.shape)
+    idx[junk < 0.05] = -1
+    idx[(junk >= 0.05) & (junk < 0.07)] = N + 5
+    if K > 1:
+        dup_rows = rng.random(S) < 0.3
+        idx[0, dup_rows, K - 1] = idx[0, dup_rows, 0]
+        idx[0, dup_rows, K // 2] = idx[0, dup_rows, 0]
+    dv = rng.standard_normal((1, S, K)).astype(np.float32)
+    _say(f"[gpu] indexer_topk_bwd ragged K={K} N={N}")
+    ds = sd.indexer_topk_bwd(torch.from_numpy(dv).to(dev), torch.from_numpy(idx).to(dev), N)
+    torch.cuda.synchronize()
+    ref = oracle.indexer_topk_bwd(dv, idx, N)
+    got = ds.reshape(-1, N).cpu().numpy().astype(np.float64)
+    # m float32 additions in slot order err by at most m 2^-24 times the sum of the magnitudes
+    mag = oracle.indexer_topk_bwd(np.abs(dv), idx, N)
+    cnt = oracle.indexer_topk_bwd(np.ones_like(dv), idx, N)
+    assert np.all(np.abs(got - ref) <= cnt * 2.0 ** -24 * mag)
+    valid = (idx[0] >= 0) & (idx[0] < N)
+    nodup = np.array([len(np.unique(r[v])) == v.sum() for r, v in zip(idx[0], valid)])
+    np.testing.assert_array_equal(got[nodup], ref[nodup].astype(np.float32).astype(np.float64))
+
+
 def test_selection_feeds_the_layer_and_its_gradient_reaches_the_scores():
     """The chain the loss runs: scores -> indexer_topk -> (idx, student logits) -> fused target
     and KL -> gradient on the logits -> indexer_topk_bwd -> gradient on the scores.  Checked

@@ -25,7 +25,8 @@ HOT = [
     ("distill_kl.hip", "distill_kl_kernelILi4ELi4E", 1),                        # KL, K = 1024
     ("indexer_topk.hip", "indexer_topk_kernelILi16E", 1),                       # top-k, N = 1024
     ("indexer_topk.hip", "indexer_topk_kernelILi32E", 1),                       # top-k, N = 2048
-    ("indexer_topk.hip", "indexer_topk_bwd_kernel", 1),
+    ("indexer_topk.hip", "indexer_topk_bwd_kernelILi8E", 1),                    # top-k scatter, K = 512
+    ("indexer_topk.hip", "indexer_topk_bwd_kernelILi16E", 1),                   # top-k scatter, K = 1024
     ("compressor_pool.hip", "compressor_pool_kernelILi0ELi4ELi1ELi2E", 1),      # CSA compressor, ratio 4
     ("compressor_pool.hip", "compressor_pool_bwd_kernelILi0ELi4ELi1ELi2E", 1),
 ]

@@ -11,8 +11,9 @@
 //
 // Mapping.  One workgroup per token, NW waves.  The token's queries (all heads) are
 // staged once in LDS.  The valid slots of the row are compacted (stable, slot order) into
-// a list in LDS; 16-slot tiles of that list are dealt round-robin to the waves, so invalid
-// (-1) slots cost no MFMA work wherever they sit.  Each wave gathers its rows from L2 in
+// a list in LDS; 16-slot tiles of that list are dealt to the waves (in pairs when the window
+// part is computed here too, else round-robin), so invalid (-1) slots cost no MFMA work
+// wherever they sit.  Each wave gathers its rows from L2 in
 // 128-byte pieces (8 consecutive lanes on a row, the layout the memory pipeline merges),
 // regroups them into MFMA operand fragments with one select and one ds_bpermute per dword, and
 // accumulates
@@ -359,20 +360,55 @@ __device__ __forceinline__ int compact_slots(const int32_t *idr, int K, int N, f
 }
 
 // ---- epilogue of one token, shared by the kernels below ----------------------------
-// Wave w holds slot tiles w, w+NW, ... (my of them, the rest of acc at -inf); lane
-// (g, x) = (lane/16, lane%16) holds rows 4g+i of each tile for heads 16ht+x.
+// Wave w holds my slot tiles of the compacted list, its l-th being TileMap::of(l) (the rest of
+// acc at -inf); lane (g, x) = (lane/16, lane%16) holds rows 4g+i of each tile for heads 16ht+x.
+//
+// The fused kernel deals slot tiles to the waves in pairs (tiles 2p, 2p+1 to one wave), so
+// each pass of the score loop over two tiles is full and every query fragment read from LDS
+// feeds two MFMAs; pairs go to the last wave first, as the first waves hold the window tiles.
+// The three-call kernel deals them round-robin (pairs cost it a register spill at 16 waves).
+// The l-th tile of wave w is t0 + (l/2) s2 + (l%2) s1.
+struct TileMap {
+    int t0, s1, s2;
+    __device__ __forceinline__ int of(int l) const { return t0 + (l >> 1) * s2 + (l & 1) * s1; }
+};
+
+// Round-robin dealing (tiles w, w+NW, w+2NW, ...).
+template <int NW>
+__device__ __forceinline__ TileMap slot_tiles_rr(int ntiles, int w, int &my) {
+    my = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;
+    return TileMap{w, NW, 2 * NW};
+}
+
+// Pair dealing: the tiles of wave w among ntiles and their count (one at a time for KT = 1).
+template <int KT, int NW>
+__device__ __forceinline__ TileMap slot_tiles(int ntiles, int w, int &my) {
+    if constexpr (KT == 1) {
+        my = ntiles > w ? 1 : 0;
+        return TileMap{w, 0, 0};
+    } else {
+        const int p0 = NW - 1 - w;  // this wave's pairs: p0, p0 + NW, ...
+        my = 0;
+#pragma unroll
+        for (int j = 0; j < KT / 2; ++j) {
+            const int r = ntiles - 2 * (p0 + NW * j);
+            my += r < 0 ? 0 : (r > 2 ? 2 : r);
+        }
+        return TileMap{2 * p0, 1, 2 * NW};
+    }
+}
 
 // Per-head maximum and sum of exp2 over this wave's slots (log2 domain, scale > 0),
 // published in red_m/red_s laid out [wave][head%16][head tile].  Padding rows of the
 // partial last tile (at most one per wave) are set to -inf first, so every later step
 // sees only real slots.  On return acc holds exp2(c - mloc).
 template <int HT, int KT, int NW>
-__device__ __forceinline__ void epi_stats(f32x4 (&acc)[KT][HT], float (&mloc)[HT], int my, int nv, int w, int lane,
-                                          float scale_log2, float *red_m, float *red_s) {
+__device__ __forceinline__ void epi_stats(f32x4 (&acc)[KT][HT], float (&mloc)[HT], int my, int nv, TileMap tm,
+                                          int w, int lane, float scale_log2, float *red_m, float *red_s) {
     const int x = lane & 15, prow = 4 * (lane >> 4);
 #pragma unroll
     for (int l = 0; l < KT; ++l) {
-        const int base = 16 * (w + l * NW);
+        const int base = 16 * tm.of(l);
         if (l < my && base + 16 > nv) {  // uniform: the partial tile
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -444,8 +480,8 @@ __device__ __forceinline__ void tr_step(float (&v)[16], bool hi) {
 // stores it at its slot.  nc: the natural-log nc_lse of head 16*min(g, HT-1)+x (ignored when
 // has_nc is false).
 template <int HT, int KT, int NW>
-__device__ __forceinline__ void epi_target(const f32x4 (&acc)[KT][HT], const float (&mloc)[HT], int my, int nv, int w,
-                                           int lane, int H, bool has_nc, float nc, float floor_log2, const float *red_m,
+__device__ __forceinline__ void epi_target(const f32x4 (&acc)[KT][HT], const float (&mloc)[HT], int my, int nv,
+                                           TileMap tm, int lane, int H, bool has_nc, float nc, float floor_log2, const float *red_m,
                                            const float *red_s, const int32_t *cslot, float *Tr) {
     static_assert(KT <= 4 || KT % 4 == 0, "tiles are reduced in groups of four");
     const int x = lane & 15, g = lane >> 4;
@@ -493,7 +529,7 @@ __device__ __forceinline__ void epi_target(const f32x4 (&acc)[KT][HT], const flo
         tr_step<0x141, 8>(v, (x & 4) != 0);   // row_half_mirror partner x^7
         tr_step<0x4e, 4>(v, (x & 2) != 0);    // quad_perm 2301 partner x^2
         tr_step<0xb1, 2>(v, (x & 1) != 0);    // quad_perm 1032 partner x^1
-        const int l = lg + (x >> 2), pos = 16 * (w + l * NW) + 4 * g + (x & 3);
+        const int l = lg + (x >> 2), pos = 16 * tm.of(l) + 4 * g + (x & 3);
         if (l < KT && l < my && pos < nv) Tr[cslot[pos]] = v[0];
     }
 }
@@ -514,6 +550,12 @@ struct TargetArgs {
     float *target;
 };
 
+// Window tiles of token t (16 keys each, from max(0, t-W+1) to t; at most eight for W <= 128).
+__device__ __forceinline__ int window_tiles(int W, int t) {
+    const int kf = t - W + 1 > 0 ? t - W + 1 : 0;
+    return (t - kf + 16) >> 4;
+}
+
 // Window part of the joint softmax for token t of batch b, inside the target kernel:
 // the LSE over {scale <q_h, kwin_j> : j in [max(0, t-W+1), t], seg[j] == seg[t]} plus the
 // sink, per head.  Window tiles of 16 consecutive keys starting at the first key are dealt
@@ -530,7 +572,7 @@ __device__ __forceinline__ void window_local(const TargetArgs &a, const unsigned
     constexpr int EB = Elem<DT>::bytes;
     const int S = a.S, D = a.D, nch = D >> 5;
     const int kf = t - a.W + 1 > 0 ? t - a.W + 1 : 0;
-    const int nwt = (t - kf + 16) >> 4;                                 // at most 8 (W <= 128)
+    const int nwt = window_tiles(a.W, t);
     const int myw = nwt - KWT * w >= KWT ? KWT : (nwt - KWT * w > 0 ? nwt - KWT * w : 0);  // tiles KWT*w + l
     const rsrc_t kr = make_rsrc(reinterpret_cast<const char *>(a.kwin) + (size_t)b * S * D * EB,
                                 (uint32_t)((size_t)S * D * EB));
@@ -679,9 +721,10 @@ __global__ __launch_bounds__(NW * 64, (waves_per_eu<DT, HT, KT>())) void distill
         return;
     }
 
-    // 2. Scores of this wave's slot tiles: tiles w, w+NW, w+2NW, ... of the compacted list.
+    // 2. Scores of this wave's slot tiles (TileMap) of the compacted list.
     const int ntiles = (nv + 15) >> 4;
-    const int my = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;
+    int my;
+    const TileMap tm = FUSED ? slot_tiles<KT, NW>(ntiles, w, my) : slot_tiles_rr<NW>(ntiles, w, my);
     const rsrc_t pr = make_rsrc(reinterpret_cast<const char *>(a.pool) + (size_t)b * N * D * EB,
                                 (uint32_t)((size_t)N * D * EB));
     // Tiles this wave does not compute stay at -inf: they drop out of the maximum and
@@ -698,7 +741,7 @@ __global__ __launch_bounds__(NW * 64, (waves_per_eu<DT, HT, KT>())) void distill
         uint32_t olo[KT], ohi[KT];
 #pragma unroll
         for (int l = 0; l < KT; ++l) {
-            const int pos = 16 * (w + l * NW) + pair_row_lane(lane);
+            const int pos = 16 * tm.of(l) + pair_row_lane(lane);
             const int r0 = (l < my && pos < nv) ? crow[pos] : crow[0];
             const int r1 = (l < my && pos + 8 < nv) ? crow[pos + 8] : crow[0];
             // 24-bit multiplies (rows < 2^24): 32-bit results, no 64-bit register pairs
@@ -722,7 +765,7 @@ __global__ __launch_bounds__(NW * 64, (waves_per_eu<DT, HT, KT>())) void distill
         uint32_t off[KT];
 #pragma unroll
         for (int l = 0; l < KT; ++l) {
-            const int pos = 16 * (w + l * NW) + (lane & 15);
+            const int pos = 16 * tm.of(l) + (lane & 15);
             const int r = (l < my && pos < nv) ? crow[pos] : crow[0];
             off[l] = (uint32_t)((r * D + 8 * (lane >> 4)) * EB);
         }
@@ -739,10 +782,10 @@ __global__ __launch_bounds__(NW * 64, (waves_per_eu<DT, HT, KT>())) void distill
         lane = t & 63;
     }
     float mloc[HT];
-    epi_stats<HT, KT, NW>(acc, mloc, my, nv, w, lane, a.scale_log2, red_m, red_s);
+    epi_stats<HT, KT, NW>(acc, mloc, my, nv, tm, w, lane, a.scale_log2, red_m, red_s);
     __syncthreads();
     if constexpr (FUSED) window_done();
-    epi_target<HT, KT, NW>(acc, mloc, my, nv, w, lane, H, FUSED || a.nc_lse != nullptr, nc, a.floor_log2, red_m,
+    epi_target<HT, KT, NW>(acc, mloc, my, nv, tm, lane, H, FUSED || a.nc_lse != nullptr, nc, a.floor_log2, red_m,
                            red_s, cslot, Tr);
 }
 

@@ -14,7 +14,8 @@
 // order-preserving 32-bit keys (NaN -> 0, the smallest); the K-th largest visible key is
 // found one byte at a time, most significant first: each pass counts the visible keys that
 // share the bytes found so far into a 256-bin histogram in the wave's LDS (one atomic add per
-// key), and a suffix scan over the bins picks the next byte.  Four passes, no sort.
+// key), and a suffix scan over the bins (DPP, on the VALU) picks the next byte.  At most four
+// passes, no sort.
 // The backward is the adjoint of the gather values[k] = scores[idx[k]]: a dense row of N
 // gradients, built in LDS and streamed out with 16-byte stores.  Outputs are written with
 // streaming (non-temporal) stores: nothing reads them back here, and they measured faster.
@@ -53,16 +54,30 @@ __device__ __forceinline__ int wave_prefix(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Sum of v over this lane and every higher lane (inclusive suffix sum), on the VALU: a
+// Hillis-Steele scan inside each 16-lane row with DPP row shifts (lanes past the row's end
+// read 0), then the totals of the higher rows, read as scalars, are added.
+__device__ __forceinline__ int wave_suffix_sum(int v, int lane) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x101, 0xf, 0xf, true);  // row_shl:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x102, 0xf, 0xf, true);  // row_shl:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x104, 0xf, 0xf, true);  // row_shl:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x108, 0xf, 0xf, true);  // row_shl:8
+    const int r1 = __builtin_amdgcn_readlane(v, 16), r2 = __builtin_amdgcn_readlane(v, 32),
+              r3 = __builtin_amdgcn_readlane(v, 48);  // totals of rows 1, 2, 3
+    const int row = lane >> 4;
+    return v + (row < 1 ? r1 : 0) + (row < 2 ? r2 : 0) + (row < 3 ? r3 : 0);
+}
+
 // E: registers per lane (N <= 64 E).
 template <int E>
 __global__ __launch_bounds__(kTopkWaves * 64) void indexer_topk_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ seg, int64_t rows, int S, int N, int K, int ratio,
     int32_t *__restrict__ idx_out, float *__restrict__ val_out) {
-    __shared__ __align__(16) uint32_t hist_all[kTopkWaves][256];
+    __shared__ __align__(16) uint32_t hist_all[kTopkWaves][2][256];
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kTopkWaves + (threadIdx.x >> 6);
-    if (row >= rows) return;  // waves never meet at a workgroup barrier: each owns its histogram
-    uint32_t *hist = hist_all[threadIdx.x >> 6];
+    if (row >= rows) return;  // waves never meet at a workgroup barrier: each owns its histograms
+    uint32_t(*hists)[256] = hist_all[threadIdx.x >> 6];  // two, used by alternate passes
     const int64_t b = row / S;
     const int t = (int)(row - b * S);
     const int ncomplete = (t + 1) / ratio;           // blocks complete at t
@@ -98,26 +113,28 @@ __global__ __launch_bounds__(kTopkWaves * 64) void indexer_topk_kernel(
     if (count > K) {
         need = K;
         uint32_t hmask = 0u;
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            *reinterpret_cast<u32x4 *>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
-            wave_lds_order();
+        *reinterpret_cast<u32x4 *>(hists[0] + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 *>(hists[1] + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+        wave_lds_order();
+        for (int shift = 24, pass = 0; shift >= 0; shift -= 8, pass ^= 1) {
+            uint32_t *hist = hists[pass];  // zero: cleared before the first pass or after its last use
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 if (vis[e] && (key[e] & hmask) == tau) atomicAdd(hist + ((key[e] >> shift) & 255u), 1u);
             wave_lds_order();
             const u32x4 h = *reinterpret_cast<const u32x4 *>(hist + 4 * lane);   // bins 4*lane .. 4*lane+3
+            // cleared for the pass after next; the next pass's wait orders it before that pass
+            *reinterpret_cast<u32x4 *>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
             const int own = (int)(h[0] + h[1] + h[2] + h[3]);
-            int suf = own;  // keys in the bins of this lane and of every higher lane
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int t = __shfl_down(suf, d);
-                suf += lane + d < 64 ? t : 0;
-            }
-            // the byte's lane: the highest one whose suffix still reaches `need`
+            const int suf = wave_suffix_sum(own, lane);  // keys in the bins of this and every higher lane
+            // the byte's lane: the highest one whose suffix still reaches `need` (suf never
+            // grows with the lane, and lane 0's suffix is every counted key, at least `need`)
             const int L = __popcll(__ballot(suf >= need)) - 1;
-            const int above = __shfl(suf - own, L);   // keys in bins above lane L's four
-            const u32x4 hl = {(uint32_t)__shfl((int)h[0], L), (uint32_t)__shfl((int)h[1], L),
-                              (uint32_t)__shfl((int)h[2], L), (uint32_t)__shfl((int)h[3], L)};
+            const int above = __builtin_amdgcn_readlane(suf - own, L);   // keys in bins above lane L's four
+            const u32x4 hl = {(uint32_t)__builtin_amdgcn_readlane((int)h[0], L),
+                              (uint32_t)__builtin_amdgcn_readlane((int)h[1], L),
+                              (uint32_t)__builtin_amdgcn_readlane((int)h[2], L),
+                              (uint32_t)__builtin_amdgcn_readlane((int)h[3], L)};
             int cum = above, dig = 4 * L, inbin = 0;
 #pragma unroll
             for (int j = 3; j >= 0; --j) {

@@ -14,7 +14,8 @@
 //
 // The work is a stream over kv and score (HBM-bound; every token row is read by one or two
 // entries, the second time from L2).  Forward: one thread per (entry, CPT consecutive
-// channels), an online softmax in exp2 form over the window.  Backward: one thread per
+// channels), a softmax in exp2 form over the window (all positions in registers for windows
+// of up to 16, an online pass for larger ones).  Backward: one thread per
 // (chunk of kChunk entries, CPT channels), 64 channel groups to a wave and kBwdWaves
 // consecutive chunks to a workgroup; for every window it recomputes the weights and the
 // pooled value, then writes each block's dkv and dscore once (with overlap a block takes
@@ -117,6 +118,43 @@ __global__ __launch_bounds__(kPoolThreads) void compressor_pool_kernel(const Poo
     const int d0 = g * CPT;
     const int32_t *sg = a.seg ? a.seg + b * a.S : nullptr;
     const int32_t seg_last = sg ? sg[R * n + R - 1] : 0;
+    if constexpr (Wc <= 16) {
+        // Small windows: every position's loads are issued at once (absent positions read a
+        // clamped row whose values are replaced), then the maximum, the exponentials and the sums.
+        float l[Wc][CPT], k[Wc][CPT];
+#pragma unroll
+        for (int i = 0; i < Wc; ++i) {
+            const int j = R * n - OVL * R + i;
+            const bool pr = present<R, OVL>(sg, n, i, seg_last);
+            const int64_t row = b * a.S + (j > 0 ? j : 0);
+            float s[CPT], ap[CPT];
+            load_ch<DT, CPT>(a.score, row * a.D + d0, s);
+            load_ch<DT, CPT>(a.kv, row * a.D + d0, k[i]);
+            load_f32<CPT>(a.ape + (int64_t)i * a.D + d0, ap);
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {  // an absent row's values never reach the sums, NaN included
+                l[i][c] = pr ? (s[c] + ap[c]) * kLog2e : -INFINITY;
+                k[i][c] = pr ? k[i][c] : 0.f;
+            }
+        }
+        float out[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            float m = l[Wc - 1][c];  // the entry's last token is always present
+#pragma unroll
+            for (int i = 0; i < Wc - 1; ++i) m = fmaxf(m, l[i][c]);
+            float den = 0.f, num = 0.f;
+#pragma unroll
+            for (int i = 0; i < Wc; ++i) {
+                const float e = fast_exp2(l[i][c] - m);  // 0 at absent positions
+                den += e;
+                num = fmaf(e, k[i][c], num);
+            }
+            out[c] = num / den;
+        }
+        store_f32<CPT>(a.pool + bn * a.D + d0, out);
+        return;
+    }
     float m[CPT], den[CPT], num[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
@@ -124,7 +162,7 @@ __global__ __launch_bounds__(kPoolThreads) void compressor_pool_kernel(const Poo
         den[c] = 0.f;
         num[c] = 0.f;
     }
-#pragma unroll(Wc <= 16 ? Wc : 8)
+#pragma unroll 8
     for (int i = 0; i < Wc; ++i) {
         if (!present<R, OVL>(sg, n, i, seg_last)) continue;
         const int64_t row = b * a.S + (R * n - OVL * R + i);

@@ -82,6 +82,8 @@ def test_hca_compressor():
     (1, 77, 12, 1, False, "f32", 0),
     (1, 1000, 128, 32, False, "bf16", 300),
     (1, 64, 4, 64, False, "f32", 0),
+    (1, 700, 32, 8, True, "bf16", 250),     # 16-position windows: the largest held in registers
+    (1, 520, 16, 16, False, "f32", 0),
 ], ids=lambda c: "-".join(map(str, c)))
 def test_compressor_edge_shapes(case):
     B, S, D, r, ovl, dt, L = case

@@ -94,6 +94,34 @@ def test_compressor_edge_shapes(case):
     run_case(cfg, r, ovl, seg=seg, what="edge")
 
 
+def _random_compressor_cases(n=16, seed=51515):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        ovl = bool(rng.random() < 0.5)
+        r = int(rng.choice([1, 2, 4, 8, 16] if ovl else [1, 2, 4, 8, 16, 32, 64, 128]))
+        D = 4 * int(rng.integers(1, 129))
+        S = int(rng.integers(r, 2500))
+        B = int(rng.integers(1, 3))
+        dt = "bf16" if rng.random() < 0.6 else "f32"
+        L = int(rng.choice([0, int(rng.integers(1, S + 1))]))
+        out.append((B, S, D, r, ovl, dt, L))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_compressor_cases(), ids=lambda c: "-".join(map(str, c)))
+def test_compressor_random_shapes(case):
+    """Seeded random shapes: ratios 1..128 (up to 16 with overlap), D a multiple of 4 up to
+    512, ragged S, bf16 and fp32, optional segments of arbitrary length."""
+    B, S, D, r, ovl, dt, L = case
+    cfg = synth.Config(f"cpr_{S}_{D}_{r}", 600 + (S + 3 * D + r) % 157, B=B, S=S, H=1, D=D, N=max(S // r, 1), K=1,
+                       W=1, dtype=dt)
+    seg = None
+    if L:
+        seg = (np.arange(S) // L).astype(np.int32)[None].repeat(B, 0)
+    run_case(cfg, r, ovl, seg=seg, what="random")
+
+
 def test_compressor_deterministic_and_segment_isolated():
     sd = _sd()
     dev = torch.device("cuda:0")

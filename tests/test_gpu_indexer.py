@@ -91,6 +91,43 @@ def test_topk_edge_shapes(case):
     check_topk(s, seg, K, ratio, "edge", rows=rows)
 
 
+def _random_topk_cases(n=16, seed=77031):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        ratio = int(rng.choice([1, 2, 4, 8, 16, 128]))
+        N = int(rng.integers(1, 4097))
+        S = int(min(max(ratio, N * ratio + int(rng.integers(-3 * ratio, 3 * ratio + 1))), 3000))
+        K = int(rng.choice([int(rng.integers(1, 65)), int(rng.integers(1, N + 1)), int(rng.integers(1, 4097))]))
+        B = int(rng.integers(1, 3))
+        if B * S * max(N, K) > 12_000_000:  # the oracle's dense scatter stays small
+            continue
+        segs = int(rng.integers(1, 4))
+        ties = bool(rng.random() < 0.4)
+        out.append((B, S, N, K, ratio, segs, ties))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_topk_cases(), ids=lambda c: "-".join(map(str, c)))
+def test_topk_random_shapes_bit_exact(case):
+    """Seeded random shapes (N up to 4096, K up to 4096, block ratios 1..128, up to three
+    segments, optionally tied scores): every row bit-exact against the oracle, selection and
+    scatter."""
+    B, S, N, K, ratio, segs, ties = case
+    cfg = synth.Config(f"topk_r_{S}_{N}", 700 + (S * 7 + N) % 211, B=B, S=S, H=1, D=32, N=N, K=K, W=1, dtype="f32")
+    s = synth.student_scores(cfg, ties=ties).numpy()
+    seg = None
+    if segs > 1:
+        seg = np.minimum(np.arange(S) * segs // S, segs - 1).astype(np.int32)[None].repeat(B, 0)
+    idx, val = check_topk(s, seg, K, ratio, "random")
+    sd = _sd()
+    dv = torch.from_numpy(np.random.default_rng(S + N + K).standard_normal((B, S, K)).astype(np.float32))
+    ds = sd.indexer_topk_bwd(dv.to(torch.device("cuda:0")), idx, N)
+    torch.cuda.synchronize()
+    ref = oracle.indexer_topk_bwd(dv, idx.cpu(), N).astype(np.float32)
+    np.testing.assert_array_equal(ds.reshape(-1, N).cpu().numpy(), ref)
+
+
 def test_topk_bwd_scatter_bit_exact_and_duplicates():
     sd = _sd()
     dev = torch.device("cuda:0")
